@@ -1,0 +1,303 @@
+"""Plain fp64 CPU oracle of the LightningIndexer forward pass.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this module:
+only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use it. It shares no code with the HIP path (no decoders,
+no tables, no helpers); its inputs are the raw host arrays of a seeded
+workload, read by attribute.
+
+What it computes (all pages agree on the formula; the MindSpore
+``mindspore.ops.lightning_indexer`` page states it most cleanly, in its
+formula block; the CANN LightningIndexerV2 guide gives the same three-step
+description in "三步计算流程"; the VllmQuantLightningIndexer README gives the
+quantised form in its "功能说明" formula):
+
+    for every query token, every visible key j:
+        s_j = sum_g  W[g] * ReLU( Q_index[g] . K_index[j] )            (plain)
+        s_j = sum_g  W[g] * ReLU( Sq[g] * Sk[j] * (Qc[g] . Kc[j]) )    (quantised)
+    Indices = Top-k over the visible keys of s.
+
+Steps, in the order of the TileLang guide's ``index_golden`` (dot products
+per head, ReLU, multiply by the per-head weight, sum over the heads, top-k
+with largest first and sorted output):
+
+1. actual lengths per batch: S_q, S_k (BSND: seqused or the padded dim;
+   TND: cu_seqlens differences; PA_BSND: seqused_k);
+2. visible keys of query row i: all S_k for sparse_mode 0; for sparse_mode 3
+   (right-down causal) key j is visible iff j <= i + S_k - S_q, i.e. the
+   first clamp(i + 1 + S_k - S_q, 0, S_k) keys;
+3. decode the stored codes to float64 exactly (own IEEE-field decoders);
+4. s_j in float64 as above (a float64 matrix product is the dot step);
+5. order the visible keys by (s desc, j asc), keep the first m = min(k, n);
+6. sparse_indices = those j then -1; sparse_values = float32(s_j) then -inf
+   (fill values from the LightningIndexerV2 guide's constraint list).
+
+Readings where the pages are silent (all listed in the design notes):
+lowest index wins ties; output sorted by score; indices are 0-based positions
+within the sequence; query rows past the actual query length are all padding;
+sparse_values are float32.
+
+Every function here is pinned by ``tests/test_oracle.py`` against closed
+forms, hand-worked examples, brute force or library routines.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Optional, Tuple
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Step 3: decoders, written from the IEEE / OCP field definitions
+# ---------------------------------------------------------------------------
+
+
+def decode_f16(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits."""
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = np.ldexp(1.0 + f / 1024.0, (e - 15).astype(np.int32))
+    sub = np.ldexp(f / 1024.0, -14)
+    special = np.where(f == 0, np.inf, np.nan)
+    mag = np.where(e == 0, sub, np.where(e == 31, special, normal))
+    return sign * mag
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits."""
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    f = (b & 0x7F).astype(np.float64)
+    normal = np.ldexp(1.0 + f / 128.0, (e - 127).astype(np.int32))
+    sub = np.ldexp(f / 128.0, -126)
+    special = np.where(f == 0, np.inf, np.nan)
+    mag = np.where(e == 0, sub, np.where(e == 255, special, normal))
+    return sign * mag
+
+
+def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 fraction bits.
+
+    No infinities; S.1111.111 is NaN; the largest finite value is 448.
+    """
+    b = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    f = (b & 0x7).astype(np.float64)
+    normal = np.ldexp(1.0 + f / 8.0, (e - 7).astype(np.int32))
+    sub = np.ldexp(f / 8.0, -6)
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where((e == 15) & (f == 7), np.nan, mag)
+    return sign * mag
+
+
+def decode_i8(codes: np.ndarray) -> np.ndarray:
+    return np.asarray(codes).astype(np.int8).astype(np.float64)
+
+
+def decode_f32(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+_DECODERS = {
+    "f16": decode_f16,
+    "bf16": decode_bf16,
+    "e4m3fn": decode_e4m3fn,
+    "i8": decode_i8,
+    "f32": decode_f32,
+}
+
+
+def decode(arr: np.ndarray, dtype: str) -> np.ndarray:
+    return _DECODERS[dtype](arr)
+
+
+# ---------------------------------------------------------------------------
+# Steps 1-2: lengths and the visibility rule
+# ---------------------------------------------------------------------------
+
+
+def batch_lengths(wl) -> List[Tuple[int, int]]:
+    """Actual (S_q, S_k) per batch, from the length inputs the pages define."""
+    out = []
+    for b in range(wl.B):
+        if wl.layout_q == "TND":
+            sq = int(wl.cu_seqlens_q[b + 1]) - int(wl.cu_seqlens_q[b])
+        elif wl.seqused_q is not None:
+            sq = int(wl.seqused_q[b])
+        else:
+            sq = int(wl.q.shape[1])
+        if wl.layout_k == "TND":
+            sk = int(wl.cu_seqlens_k[b + 1]) - int(wl.cu_seqlens_k[b])
+        elif wl.seqused_k is not None:
+            sk = int(wl.seqused_k[b])
+        else:
+            sk = int(wl.k.shape[1])
+        out.append((sq, sk))
+    return out
+
+
+def visible_count(i: int, sq: int, sk: int, mode: int) -> int:
+    """Keys visible to query row i: all of them for mode 0; the right-down
+    causal rule j <= i + (S_k - S_q) for mode 3."""
+    if i >= sq:
+        return 0
+    if mode == 0:
+        return sk
+    if mode == 3:
+        return max(0, min(sk, i + 1 + sk - sq))
+    raise ValueError(f"sparse_mode {mode} is not defined")
+
+
+# ---------------------------------------------------------------------------
+# Step 3: per-batch operand gathering
+# ---------------------------------------------------------------------------
+
+
+def _query_block(wl, b: int, rows: np.ndarray):
+    """Decoded query rows (len(rows), N1, D), weights (len(rows), N1) and
+    query dequant scales (len(rows), N1) or None, for positions `rows` of batch b."""
+    if wl.layout_q == "TND":
+        r = int(wl.cu_seqlens_q[b]) + rows
+        qc, wc = wl.q[r], wl.w[r]
+        qs = wl.q_scale[r] if wl.q_scale is not None else None
+    else:
+        qc, wc = wl.q[b, rows], wl.w[b, rows]
+        qs = wl.q_scale[b, rows] if wl.q_scale is not None else None
+    q = decode(qc, wl.qk_dtype)
+    w = decode(wc, wl.w_dtype)
+    s = decode_f32(qs) if qs is not None else None
+    return q, w, s
+
+
+def _key_block(wl, b: int, sk: int):
+    """Decoded keys (S_k, N2, D) of batch b in logical order, plus key dequant
+    scales (S_k, N2) or None. PA_BSND: key j lives in physical block
+    block_table[b, j // block_size], row j % block_size."""
+    j = np.arange(sk)
+    if wl.layout_k == "TND":
+        r = int(wl.cu_seqlens_k[b]) + j
+        kc = wl.k[r]
+        ks = wl.k_scale[r] if wl.k_scale is not None else None
+    elif wl.layout_k == "BSND":
+        kc = wl.k[b, :sk]
+        ks = wl.k_scale[b, :sk] if wl.k_scale is not None else None
+    elif wl.layout_k == "PA_BSND":
+        bs = int(wl.k.shape[1])
+        blk = wl.block_table[b, j // bs]
+        kc = wl.k[blk, j % bs]
+        ks = wl.k_scale[blk, j % bs] if wl.k_scale is not None else None
+    else:
+        raise ValueError(wl.layout_k)
+    k = decode(kc, wl.qk_dtype)
+    s = decode_f32(ks) if ks is not None else None
+    return k, s
+
+
+# ---------------------------------------------------------------------------
+# Step 4: scores, Step 5: ordering
+# ---------------------------------------------------------------------------
+
+
+def row_scores(q: np.ndarray, w: np.ndarray, k: np.ndarray,
+               q_scale: Optional[np.ndarray] = None,
+               k_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """s_j = sum_g w[g] * ReLU(x[g, j]) for one query row and one KV head.
+
+    q: (G, D) decoded query heads, w: (G,), k: (n, D) decoded keys.
+    Quantised inputs: x[g, j] = q_scale[g] * k_scale[j] * (q[g] . k[j]),
+    i.e. ReLU is applied after dequantisation, as in the quantised formula.
+    """
+    x = q @ k.T                                    # (G, n) float64
+    if q_scale is not None:
+        x = (q_scale[:, None] * k_scale[None, :]) * x
+    return w @ np.maximum(x, 0.0)
+
+
+def topk_order(s: np.ndarray, k: int) -> np.ndarray:
+    """Positions of the k largest entries of s, by (score desc, index asc)."""
+    n = s.shape[0]
+    order = np.lexsort((np.arange(n), -s))
+    return order[: min(k, n)]
+
+
+# ---------------------------------------------------------------------------
+# Driver
+# ---------------------------------------------------------------------------
+
+
+def all_rows(wl) -> List[Tuple[int, int]]:
+    """Every output row as (batch, position)."""
+    rows = []
+    for b in range(wl.B):
+        n = (int(wl.cu_seqlens_q[b + 1]) - int(wl.cu_seqlens_q[b])
+             if wl.layout_q == "TND" else int(wl.q.shape[1]))
+        rows.extend((b, i) for i in range(n))
+    return rows
+
+
+def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool = False,
+        row_block: int = 16) -> Dict[str, object]:
+    """Oracle outputs for `rows` ((b, i) pairs; all rows when None).
+
+    Returns a dict with
+      'rows'    : list of (b, i)
+      'indices' : int32 (R, N2, k)
+      'values'  : float32 (R, N2, k)
+      'scores'  : (if want_scores) list over rows of lists over N2 of float64
+                  arrays holding s_j for every visible key j.
+    """
+    rows = list(all_rows(wl) if rows is None else rows)
+    kk = wl.sparse_count
+    N2, G = wl.N2, wl.N1 // wl.N2
+    R = len(rows)
+    idx = np.full((R, N2, kk), -1, np.int32)
+    val = np.full((R, N2, kk), -np.inf, np.float32)
+    scores: List[List[np.ndarray]] = [[np.zeros(0)] * N2 for _ in range(R)]
+    lengths = batch_lengths(wl)
+
+    by_batch: Dict[int, List[int]] = {}
+    for r, (b, i) in enumerate(rows):
+        by_batch.setdefault(b, []).append(r)
+    for b, rlist in by_batch.items():
+        sq, sk = lengths[b]
+        live = [r for r in rlist if rows[r][1] < sq and
+                visible_count(rows[r][1], sq, sk, wl.sparse_mode) > 0]
+        if not live:
+            continue
+        keys, kscale = _key_block(wl, b, sk)
+        for c in range(0, len(live), row_block):
+            chunk = live[c:c + row_block]
+            pos = np.array([rows[r][1] for r in chunk])
+            q, w, qs = _query_block(wl, b, pos)
+            for t, r in enumerate(chunk):
+                n = visible_count(int(pos[t]), sq, sk, wl.sparse_mode)
+                for h in range(N2):
+                    g = slice(h * G, (h + 1) * G)
+                    s = row_scores(q[t, g], w[t, g], keys[:n, h],
+                                   None if qs is None else qs[t, g],
+                                   None if kscale is None else kscale[:n, h])
+                    order = topk_order(s, kk)
+                    m = order.shape[0]
+                    idx[r, h, :m] = order
+                    val[r, h, :m] = s[order].astype(np.float32)
+                    if want_scores:
+                        scores[r][h] = s
+    out: Dict[str, object] = {"rows": rows, "indices": idx, "values": val}
+    if want_scores:
+        out["scores"] = scores
+    return out
+
+
+def run_full(wl) -> Tuple[np.ndarray, np.ndarray]:
+    """Whole-problem outputs shaped like the operator's: (B,S1,N2,k) for BSND
+    queries, (T1,N2,k) for TND."""
+    o = run(wl)
+    idx, val = o["indices"], o["values"]
+    if wl.layout_q == "BSND":
+        shape = (wl.B, int(wl.q.shape[1]), wl.N2, wl.sparse_count)
+        return idx.reshape(shape), val.reshape(shape)
+    return idx, val
