@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of the LightningIndexer hot path on one MI355X.
+
+One step = one full pass of the hot path (score kernel + top-k kernel, i.e.
+li_score then li_topk through the C ABI) over one batch of seeded synthetic
+input already resident in HBM. The default workload is the 8K causal prefill
+(B=1, S1=S2=8192, N1=64, N2=1, D=128, bf16 q/k, bf16 weights, k=2048,
+right-down causal, BSND); the other seeded workloads can be selected with
+--workload.
+
+Prints ONE JSON line. `value` is indexed query tokens per second; the line
+also carries the score kernel's TFLOP/s against the MFMA peak (or its GB/s
+against HBM when the workload is bandwidth-bound), the top-k kernel's GB/s,
+a `roofline` object for the dominant kernel (timed with HIP events on the
+stream it runs on) and a `cpu_baseline` object: the fp64 CPU oracle timed on a
+bounded random sample of the same rows on this host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "indexed query tokens/s + score TFLOP/s (% MFMA peak), S=8K causal prefill"
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "e4m3fn": 5000.0, "i8": 5000.0}
+PEAK_HBM_GBS = 8000.0
+SCORE_SOURCES = ("sparse_attention_top_amd/csrc/li_score.hip",
+                 "sparse_attention_top_amd/csrc/li_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_score_bytes(wl):
+    """Bytes the score kernel must move at least once: Q, W, scales, each key of
+    each sequence once, and one float32 per visible pair written."""
+    es = 1 if wl.qk_dtype in ("e4m3fn", "i8") else 2
+    ws = 4 if wl.w_dtype == "f32" else 2
+    rows = int(sum(int(x) for x in wl.seqlens_q))
+    keys = int(sum(int(x) for x in wl.seqlens_k))
+    b = rows * wl.N1 * (wl.D * es + ws) + keys * wl.N2 * wl.D * es
+    if wl.quant:
+        b += rows * wl.N1 * 4 + keys * wl.N2 * 4
+    return b + 4 * wl.visible_pairs()
+
+
+def cpu_baseline(wl, seconds, seed=1234):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import li_oracle as O
+    rows = [(b, i) for b in range(wl.B) for i in range(int(wl.seqlens_q[b]))]
+    order = np.random.default_rng(seed).permutation(len(rows))
+    done, t0 = 0, time.perf_counter()
+    chunk = 16
+    while done < len(rows) and time.perf_counter() - t0 < seconds:
+        sel = [rows[j] for j in order[done:done + chunk]]
+        O.run(wl, rows=sel)
+        done += len(sel)
+    el = time.perf_counter() - t0
+    threads = [t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"]
+    return {"value": done / el, "unit": "tokens/s", "cores": int(max(threads or [1])),
+            "kind": "oracle",
+            "sample": f"{done} query rows drawn uniformly at random (seed {seed}) from the "
+                      f"{len(rows)} rows of the same workload, {el:.1f} s of fp64 oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsa_prefill")
+    ap.add_argument("--return-value", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the indexer on one GPU only; multi-GPU runs are not part "
+              "of this build (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_top_amd import binding as B
+    from sparse_attention_top_amd import indexer as I
+    from sparse_attention_top_amd import synth
+
+    if args.workload not in synth.CONFIGS:
+        sys.exit(f"unknown workload {args.workload}; choose from {list(synth.CONFIGS)}")
+    t_gen = time.perf_counter()
+    wl = synth.CONFIGS[args.workload]()
+    print(f"[bench] generated {args.workload} in {time.perf_counter() - t_gen:.1f}s", flush=True,
+          file=sys.stderr)
+    dev = "cuda"
+    dw = I.upload(wl, dev, return_value=args.return_value)
+    plan = I.make_plan(dw.problem, dw.lengths, dev)
+    p = dw.problem
+    shape = I.output_shape(p)
+    idx = torch.empty(shape, dtype=torch.int32, device=dev)
+    val = torch.empty(shape if p.return_value else (0,), dtype=torch.float32, device=dev)
+    inp = dw.inputs()
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+    mh, md, ws, wsb = plan.meta_host, int(plan.meta_dev.data_ptr()), int(plan.ws.data_ptr()), \
+        plan.ws_bytes
+    ip, vp = int(idx.data_ptr()), (int(val.data_ptr()) if p.return_value else 0)
+
+    def score():
+        B.li_score(p, inp, mh, md, ws, wsb, sh)
+
+    def topk():
+        B.li_topk(p, mh, md, ws, wsb, ip, vp, sh)
+
+    for _ in range(args.warmup):
+        score()
+        topk()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", flush=True, file=sys.stderr)
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(K):
+        ev[s][0].record(stream)
+        score()
+        ev[s][1].record(stream)
+        topk()
+        ev[s][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    score_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    topk_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    ms_per_step = total_ms / K
+    print(f"[bench] timed {K} steps: {ms_per_step:.3f} ms/step (score {score_ms:.3f}, "
+          f"top-k {topk_ms:.3f})", flush=True, file=sys.stderr)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: 3 x 1 GiB device copy done", flush=True,
+              file=sys.stderr)
+
+    rows = wl.num_rows
+    pairs = wl.visible_pairs()
+    flops = 2.0 * wl.N1 * wl.D * pairs
+    score_tflops = flops / (score_ms * 1e-3) / 1e12
+    sbytes = algorithmic_score_bytes(wl)
+    score_gbs = sbytes / (score_ms * 1e-3) / 1e9
+    kk = wl.sparse_count
+    tbytes = 4 * pairs + rows * wl.N2 * kk * (8 if p.return_value else 4)
+    topk_gbs = tbytes / (topk_ms * 1e-3) / 1e9
+    peak_mfma = PEAK_MFMA_TFLOPS[wl.qk_dtype]
+    ridge = peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
+    hbm_bound = flops / sbytes < ridge
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_digest") == source_digest(SCORE_SOURCES) and \
+                tr.get("workload") == args.workload:
+            traffic = tr.get("bytes_per_launch")
+    if hbm_bound:
+        roof = {"kernel": "score_kernel", "bound": "hbm", "achieved": round(score_gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(score_gbs / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": sbytes}
+    else:
+        roof = {"kernel": "score_kernel", "bound": "mfma", "achieved": round(score_tflops, 1),
+                "peak": peak_mfma, "unit": "TFLOP/s",
+                "frac": round(score_tflops / peak_mfma, 4), "traffic": traffic,
+                "algorithmic_flops": flops}
+
+    out = {
+        "metric": METRIC,
+        "value": round(rows / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.qk_dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": wl.B, "S1": wl.S1, "S2": wl.S2, "N1": wl.N1,
+                   "N2": wl.N2, "D": wl.D, "layout_q": wl.layout_q, "layout_k": wl.layout_k,
+                   "sparse_count": kk, "sparse_mode": wl.sparse_mode,
+                   "return_value": bool(p.return_value), "query_rows": rows,
+                   "visible_pairs": pairs, "parallelism": "single GPU"},
+        "score_tflops": round(score_tflops, 1),
+        "score_frac_mfma_peak": round(score_tflops / peak_mfma, 4),
+        "score_ms": round(score_ms, 4),
+        "topk_ms": round(topk_ms, 4),
+        "topk_gbs": round(topk_gbs, 1),
+        "topk_frac_hbm_peak": round(topk_gbs / PEAK_HBM_GBS, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", flush=True, file=sys.stderr)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,118 @@
+// Internal definitions shared by the host side of the library and its kernels:
+// the metadata (task table) layout, score-kernel variants, kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/li.h"
+
+namespace li {
+
+// ---------------------------------------------------------------------------
+// Task table written by li_metadata (host), read by the kernels (device).
+//
+//   [MetaHeader][BatchRec x batch][WorkItem x num_items]
+//
+// Each BatchRec describes one sequence; each WorkItem is one workgroup of the
+// score kernel: query rows [q0, q0 + tile_q) of sequence b against keys
+// [k0, k1). Items are sorted by descending visible-pair count.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kMetaMagic = 0x444D494Cu;  // "LIMD"
+constexpr uint32_t kMetaVersion = 1;
+
+struct MetaHeader {
+  uint32_t magic;
+  uint32_t version;
+  uint64_t problem_hash;   // hash of the li_problem fields that shape the work
+  int32_t batch;
+  int32_t num_items;
+  int64_t num_rows;        // output rows: B*S1 (BSND) or T1 (TND)
+  int32_t variant;         // score-kernel variant (ScoreVariant)
+  int32_t tile_q;          // query rows per work item
+  int32_t key_chunk;       // keys per work item (upper bound)
+  int32_t num_cus;
+  int64_t ws_floats;       // workspace size in floats
+  int64_t visible_pairs;   // sum over rows of visible keys
+  uint64_t off_batches;    // byte offset of the BatchRec array
+  uint64_t off_items;      // byte offset of the WorkItem array
+  int32_t max_sk;
+  int32_t max_sq;
+  int32_t reserved[10];
+};
+static_assert(sizeof(MetaHeader) == 128, "header size");
+
+struct BatchRec {
+  int64_t ws_off;   // first workspace float of the sequence
+  int32_t row_base; // first output row == first q / w row of the sequence
+  int32_t k_base;   // first key row (TND: cu_seqlens_k[b]; BSND: b*S2; PA: 0)
+  int32_t s_q;      // actual query length
+  int32_t s_k;      // actual key length
+  int32_t ld;       // workspace row stride in floats (multiple of 4)
+  int32_t rows;     // output rows allotted to the sequence (S1 for BSND, s_q for TND)
+};
+static_assert(sizeof(BatchRec) == 32, "batch record size");
+
+struct WorkItem {
+  int32_t b, q0, k0, k1;
+};
+static_assert(sizeof(WorkItem) == 16, "work item size");
+
+// Score-kernel variants: waves along query rows (WQ) x waves along keys (WK),
+// 8 waves per workgroup, KT keys staged in LDS per step.
+enum ScoreVariant : int32_t {
+  kVarPrefill = 0,  // WQ=8, WK=1: 8 query rows share each staged key tile
+  kVarMid = 1,      // WQ=4, WK=2
+  kVarDecode = 2,   // WQ=2, WK=4: 2 query rows, waves split the keys
+};
+constexpr int kVariantTileQ[3] = {8, 4, 2};
+constexpr int kVariantTileK[3] = {64, 128, 128};
+
+// ---------------------------------------------------------------------------
+// Kernel arguments
+// ---------------------------------------------------------------------------
+struct ScoreArgs {
+  const uint8_t* q;
+  const uint8_t* k;
+  const void* w;
+  const float* q_scale;
+  const float* k_scale;
+  const int32_t* block_table;
+  const BatchRec* batches;
+  const WorkItem* items;
+  float* ws;
+  int64_t k_block_stride;  // elements between paged blocks
+  int64_t num_blocks;      // paged blocks; ids outside [0, num_blocks) read as zero keys
+  int32_t n1;              // query heads (== G since N2 == 1)
+  int32_t layout_k;
+  int32_t dtype_w;
+  int32_t block_size;
+  int32_t max_blocks;
+  int32_t sparse_mode;
+};
+
+struct TopkArgs {
+  const float* ws;
+  const BatchRec* batches;
+  int32_t* out_idx;
+  float* out_val;          // may be null
+  int64_t num_rows;
+  int32_t batch;
+  int32_t k;
+  int32_t sparse_mode;
+};
+
+// Host launchers (defined next to their kernels).
+hipError_t launch_score(const li_problem& p, int variant, int num_items, const ScoreArgs& a,
+                        hipStream_t s);
+hipError_t launch_topk(const li_problem& p, const TopkArgs& a, hipStream_t s);
+
+// Visible keys of query row i (i < s_q) of a sequence with lengths (s_q, s_k).
+__host__ __device__ inline int32_t visible_keys(int32_t i, int32_t s_q, int32_t s_k, int32_t mode) {
+  if (mode == 0) return s_k;
+  int64_t v = (int64_t)i + 1 + (int64_t)s_k - (int64_t)s_q;
+  return v < 0 ? 0 : (v > s_k ? s_k : (int32_t)v);
+}
+
+}  // namespace li

@@ -1,0 +1,104 @@
+"""GPU-vs-oracle acceptance rule for one indexer output row.
+
+Let s be the oracle's float64 scores of the row's visible keys (n of them),
+m = min(k, n), s_(k) the k-th largest score, s_(1) the largest, and
+tau = tol * max(|s_(k)|, 2^-6 * |s_(1)|) (tol = 1e-3 for fp16/bf16 inputs,
+2e-2 for fp8/int8). The GPU row G is accepted iff
+  1. its first m entries are distinct visible keys and the rest are -1;
+  2. every j in G has s_j >= s_(k) - tau;
+  3. every visible j with s_j > s_(k) + tau is in G;
+  4. consecutive entries are ordered by score within tau;
+  5. returned values v_j satisfy |v_j - s_j| <= tol * max(|s_j|, 2^-6 |s_(1)|),
+     are non-increasing, and the tail holds -inf.
+Rules 2-3 make G equal the oracle's set whenever s_(k) and s_(k+1) are more
+than tau apart; inside that band any choice whose oracle score is within tau
+of the k-th is accepted. Rows that see at most k keys must return all of them.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+TOL = {"f16": 1e-3, "bf16": 1e-3, "e4m3fn": 2e-2, "i8": 2e-2}
+
+
+class RowStats:
+    def __init__(self):
+        self.rows = 0
+        self.exact_set = 0
+        self.in_band = 0
+        self.all_keys = 0
+
+    def __repr__(self):
+        return (f"rows={self.rows} exact_set={self.exact_set} tie_band={self.in_band} "
+                f"all_keys={self.all_keys}")
+
+
+def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: int,
+              tol: float, oidx: Optional[np.ndarray] = None,
+              stats: Optional[RowStats] = None, where: str = "") -> None:
+    n = s.shape[0]
+    m = min(k, n)
+    gidx = np.asarray(gidx).astype(np.int64)
+    assert gidx.shape == (k,), f"{where}: bad row shape {gidx.shape}"
+    head, tail = gidx[:m], gidx[m:]
+    assert (tail == -1).all(), f"{where}: tail must be -1 (m={m}), got {tail[:8]}"
+    assert ((head >= 0) & (head < n)).all(), \
+        f"{where}: index outside [0,{n}): {head[(head < 0) | (head >= n)][:8]}"
+    assert np.unique(head).shape[0] == m, f"{where}: duplicate indices"
+    if stats is not None:
+        stats.rows += 1
+    if m == 0:
+        if gval is not None:
+            assert np.isneginf(gval).all(), f"{where}: values of an empty row must be -inf"
+        return
+    srt = np.sort(s)[::-1]
+    s1 = abs(srt[0])
+    floor = 2.0 ** -6 * s1
+    if n <= k:
+        assert np.array_equal(np.sort(head), np.arange(n)), f"{where}: must return every key"
+        tau = tol * max(abs(srt[-1]), floor)
+        if stats is not None:
+            stats.all_keys += 1
+    else:
+        sk = srt[k - 1]
+        tau = tol * max(abs(sk), floor)
+        sel = s[head]
+        bad = sel < sk - tau
+        assert not bad.any(), f"{where}: picked keys below the k-th score band: " \
+                              f"{head[bad][:5]} s={sel[bad][:5]} kth={sk} tau={tau}"
+        must = np.nonzero(s > sk + tau)[0]
+        missing = np.setdiff1d(must, head)
+        assert missing.size == 0, f"{where}: missing clear winners {missing[:5]}"
+        if stats is not None:
+            if oidx is not None and np.array_equal(np.sort(head), np.sort(oidx[:m])):
+                stats.exact_set += 1
+            else:
+                stats.in_band += 1
+    # ordering by score (within the band width)
+    sh = s[head]
+    band = tol * np.maximum(np.abs(sh), floor)
+    assert (sh[1:] <= sh[:-1] + band[:-1] + band[1:]).all(), f"{where}: not sorted by score"
+    if gval is not None:
+        gval = np.asarray(gval, dtype=np.float64)
+        v, vt = gval[:m], gval[m:]
+        assert np.isneginf(vt).all(), f"{where}: value tail must be -inf"
+        err = np.abs(v - sh)
+        lim = tol * np.maximum(np.abs(sh), floor)
+        assert (err <= lim).all(), f"{where}: values off by up to {err.max():.3g} " \
+                                   f"(limit {lim[np.argmax(err - lim)]:.3g})"
+        assert (np.diff(v) <= 0).all(), f"{where}: values not non-increasing"
+
+
+def check_rows(gidx_rows: np.ndarray, gval_rows: Optional[np.ndarray], oracle_out: dict,
+               k: int, tol: float, label: str = "") -> RowStats:
+    """gidx_rows / gval_rows: (R, N2, k) arrays aligned with oracle_out['rows']."""
+    st = RowStats()
+    for r, (b, i) in enumerate(oracle_out["rows"]):
+        for h in range(gidx_rows.shape[1]):
+            check_row(gidx_rows[r, h], None if gval_rows is None else gval_rows[r, h],
+                      oracle_out["scores"][r][h], k, tol,
+                      oidx=oracle_out["indices"][r, h], stats=st,
+                      where=f"{label} row (b={b}, i={i})")
+    return st

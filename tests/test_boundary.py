@@ -1,0 +1,275 @@
+"""CPU tests of the C-ABI boundary: exported symbols, argument checks, the
+metadata partitioner and workspace sizing. No compute call is made here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_attention_top_amd import binding as B
+from sparse_attention_top_amd import indexer as I
+from sparse_attention_top_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_attention_top_amd import build
+        build.build(verbose=False)
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "li.h")).read()
+    names = sorted(set(re.findall(r"^\s*(?:li_status|const char\*|int32_t)\s+(li_\w+)\s*\(",
+                                  hdr, re.M)))
+    assert {"li_metadata", "li_workspace_size", "li_score", "li_topk", "li_indexer",
+            "li_last_error", "li_api_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared in li.h but not exported"
+    assert B.li_api_version() == B.API_VERSION
+
+
+def _prob(**kw):
+    base = dict(layout_q="BSND", layout_k="BSND", dtype_qk="bf16", dtype_w="bf16", batch=2,
+                s1=16, s2=64, n1=64, n2=1, d=128, sparse_count=32, sparse_mode=3)
+    base.update(kw)
+    return B.make_problem(**base)
+
+
+def _status(p, lengths=None):
+    L = lengths if lengths is not None else B.make_lengths()
+    try:
+        B.li_metadata(p, L)
+        return B.OK
+    except B.LIError as e:
+        return e.status
+
+
+BAD = [
+    ("empty batch", dict(batch=0), B.ERR_EMPTY_TENSOR),
+    ("empty heads", dict(n1=0), B.ERR_EMPTY_TENSOR),
+    ("empty dim", dict(d=0), B.ERR_EMPTY_TENSOR),
+    ("empty s1", dict(s1=0), B.ERR_EMPTY_TENSOR),
+    ("empty s2", dict(s2=0), B.ERR_EMPTY_TENSOR),
+    ("negative batch", dict(batch=-1), B.ERR_INVALID_ARGUMENT),
+    ("layout pairing", dict(layout_k="TND", t2=64), B.ERR_INVALID_ARGUMENT),
+    ("bad layout", dict(layout_q=7), B.ERR_INVALID_ARGUMENT),
+    ("w dtype", dict(dtype_w="e4m3fn"), B.ERR_INVALID_ARGUMENT),
+    ("qk dtype", dict(dtype_qk="f32"), B.ERR_INVALID_ARGUMENT),
+    ("k zero", dict(sparse_count=0), B.ERR_INVALID_ARGUMENT),
+    ("k too big", dict(sparse_count=2049), B.ERR_INVALID_ARGUMENT),
+    ("mode 1", dict(sparse_mode=1), B.ERR_INVALID_ARGUMENT),
+    ("mode 2", dict(sparse_mode=2), B.ERR_INVALID_ARGUMENT),
+    ("pre_tokens", dict(pre_tokens=100), B.ERR_UNSUPPORTED),
+    ("next_tokens", dict(next_tokens=0), B.ERR_UNSUPPORTED),
+    ("n2 > 1", dict(n2=2), B.ERR_UNSUPPORTED),
+    ("n1 > 64", dict(n1=65), B.ERR_UNSUPPORTED),
+    ("d = 96", dict(d=96), B.ERR_UNSUPPORTED),
+    ("pa block 8", dict(layout_k="PA_BSND", block_size=8, num_blocks=4, max_blocks_per_seq=4),
+     B.ERR_INVALID_ARGUMENT),
+    ("pa block 24", dict(layout_k="PA_BSND", block_size=24, num_blocks=4, max_blocks_per_seq=4),
+     B.ERR_INVALID_ARGUMENT),
+    ("pa block 2048", dict(layout_k="PA_BSND", block_size=2048, num_blocks=4,
+                           max_blocks_per_seq=4), B.ERR_INVALID_ARGUMENT),
+    ("pa no blocks", dict(layout_k="PA_BSND", block_size=16, num_blocks=0, max_blocks_per_seq=4),
+     B.ERR_EMPTY_TENSOR),
+    ("pa small stride", dict(layout_k="PA_BSND", block_size=16, num_blocks=4,
+                             max_blocks_per_seq=4, k_block_stride=16), B.ERR_INVALID_ARGUMENT),
+    ("quant scale dtype", dict(dtype_qk="e4m3fn", dtype_scale="f16"), B.ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD, ids=[b[0] for b in BAD])
+def test_problem_checks(lib, name, kw, status):
+    assert _status(_prob(**kw)) == status
+    assert B.li_last_error()
+
+
+def test_reserved_and_version(lib):
+    p = _prob()
+    p.reserved[3] = 1
+    assert _status(p) == B.ERR_INVALID_ARGUMENT
+    p = _prob()
+    p.api_version = 99
+    assert _status(p) == B.ERR_INVALID_ARGUMENT
+    p = _prob()
+    p.return_value = 2
+    assert _status(p) == B.ERR_INVALID_ARGUMENT
+
+
+LEN_BAD = [
+    ("tnd without cu_seqlens_q", dict(layout_q="TND", layout_k="TND", t1=8, t2=8, batch=1),
+     dict(cu_seqlens_k=[0, 8])),
+    ("bsnd with cu_seqlens_q", dict(), dict(cu_seqlens_q=[0, 8, 16])),
+    ("bsnd with cu_seqlens_k", dict(), dict(cu_seqlens_k=[0, 8, 16])),
+    ("cu_seqlens first not 0", dict(layout_q="TND", layout_k="TND", t1=8, t2=8, batch=1),
+     dict(cu_seqlens_q=[1, 8], cu_seqlens_k=[0, 8])),
+    ("cu_seqlens decreasing", dict(layout_q="TND", layout_k="TND", t1=8, t2=8, batch=2),
+     dict(cu_seqlens_q=[0, 9, 8], cu_seqlens_k=[0, 4, 8])),
+    ("cu_seqlens total", dict(layout_q="TND", layout_k="TND", t1=8, t2=8, batch=1),
+     dict(cu_seqlens_q=[0, 7], cu_seqlens_k=[0, 8])),
+    ("seqused_q above s1", dict(), dict(seqused_q=[17, 3])),
+    ("seqused_k above s2", dict(), dict(seqused_k=[3, 65])),
+    ("seqused_k negative", dict(), dict(seqused_k=[-1, 3])),
+    ("pa without seqused_k", dict(layout_k="PA_BSND", block_size=16, num_blocks=8,
+                                  max_blocks_per_seq=4), dict()),
+    ("pa block_table too short", dict(layout_k="PA_BSND", block_size=16, num_blocks=8,
+                                      max_blocks_per_seq=4), dict(seqused_k=[65, 3])),
+    ("tnd seqused_k beyond cu", dict(layout_q="TND", layout_k="TND", t1=8, t2=8, batch=1),
+     dict(cu_seqlens_q=[0, 8], cu_seqlens_k=[0, 8], seqused_k=[9])),
+]
+
+
+@pytest.mark.parametrize("name,pk,lk", LEN_BAD, ids=[b[0] for b in LEN_BAD])
+def test_length_checks(lib, name, pk, lk):
+    assert _status(_prob(**pk), B.make_lengths(**lk)) == B.ERR_INVALID_ARGUMENT
+
+
+def test_buffer_too_small_reports_size(lib):
+    p = _prob()
+    L = B.make_lengths()
+    need = ctypes.c_size_t(0)
+    buf = np.zeros(64, np.uint8)
+    st = lib.li_metadata(ctypes.byref(p), ctypes.byref(L), 256, buf.ctypes.data, 64,
+                         ctypes.byref(need))
+    assert st == B.ERR_BUFFER_TOO_SMALL and need.value > 64
+
+
+# ---------------------------------------------------------------------------
+# task table
+# ---------------------------------------------------------------------------
+def _coverage(wl, meta):
+    """Every visible (row, key) pair is covered by exactly one work item."""
+    h, recs, items = B.parse_metadata(meta)
+    tq = int(h["tile_q"])
+    cover = {}
+    for b in range(wl.B):
+        sq, sk = int(recs[b]["s_q"]), int(recs[b]["s_k"])
+        cover[b] = np.zeros((sq, max(sk, 1)), np.int32)
+    for it in items:
+        b, q0, k0, k1 = (int(it[f]) for f in ("b", "q0", "k0", "k1"))
+        r = recs[b]
+        assert k0 < k1
+        for i in range(q0, min(q0 + tq, int(r["s_q"]))):
+            nv = wl.n_valid(b, i)
+            hi = min(nv, k1)
+            if hi > k0:
+                cover[b][i, k0:hi] += 1
+    pairs = 0
+    for b in range(wl.B):
+        for i in range(int(recs[b]["s_q"])):
+            nv = wl.n_valid(b, i)
+            assert (cover[b][i, :nv] == 1).all(), f"row ({b},{i}) not covered exactly once"
+            assert (cover[b][i, nv:] == 0).all()
+            pairs += nv
+    assert pairs == int(h["visible_pairs"]) == wl.visible_pairs()
+    return h, recs, items
+
+
+WORKLOADS = {
+    "causal": lambda: synth.build("c", layout_q="BSND", layout_k="BSND", qk_dtype="bf16",
+                                  w_dtype="bf16", N1=64, D=128, seqlens_q=[300], seqlens_k=[300],
+                                  sparse_count=64, sparse_mode=3, seed=1),
+    "nomask": lambda: synth.build("n", layout_q="BSND", layout_k="BSND", qk_dtype="f16",
+                                  w_dtype="f32", N1=32, D=64, seqlens_q=[37, 37],
+                                  seqlens_k=[500, 500], sparse_count=64, sparse_mode=0, seed=2),
+    "seqused": lambda: synth.build("u", layout_q="BSND", layout_k="BSND", qk_dtype="bf16",
+                                   w_dtype="bf16", N1=16, D=128, seqlens_q=[10, 33, 0],
+                                   seqlens_k=[100, 20, 50], S1=40, S2=120, sparse_count=8,
+                                   sparse_mode=3, seed=3),
+    "varlen": lambda: synth.build("v", layout_q="TND", layout_k="TND", qk_dtype="e4m3fn",
+                                  w_dtype="f32", N1=64, D=128, seqlens_q=[5, 0, 70, 19],
+                                  seqlens_k=[5, 0, 70, 40], sparse_count=16, sparse_mode=3,
+                                  seed=4),
+    "paged": lambda: synth.paged_decode(B=6, lo=100, hi=900, block_size=64),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_metadata_covers_every_pair_once(lib, name):
+    wl = WORKLOADS[name]()
+    dp = I.problem_of(wl)
+    meta = B.li_metadata(dp, B.make_lengths(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.seqused_q,
+                                            wl.seqused_k))
+    h, recs, items = _coverage(wl, meta)
+    assert int(h["num_rows"]) == wl.num_rows
+    # workspace rows are 16-byte aligned and long enough
+    for b in range(wl.B):
+        assert int(recs[b]["ld"]) % 4 == 0 and int(recs[b]["ld"]) >= int(recs[b]["s_k"])
+        assert int(recs[b]["ws_off"]) % 4 == 0
+    assert B.li_workspace_size(dp, meta) >= 4 * int(sum(int(r["s_q"]) * int(r["ld"])
+                                                        for r in recs))
+
+
+def test_metadata_heaviest_first_and_balanced(lib):
+    p = B.make_problem(layout_q="BSND", layout_k="BSND", dtype_qk="bf16", dtype_w="bf16",
+                       batch=1, s1=8192, s2=8192, n1=64, d=128, sparse_count=2048, sparse_mode=3)
+    meta = B.li_metadata(p, B.make_lengths())
+    h, recs, items = B.parse_metadata(meta)
+    tq = int(h["tile_q"])
+    cost = []
+    for it in items:
+        c = 0
+        for i in range(int(it["q0"]), min(int(it["q0"]) + tq, 8192)):
+            c += max(0, min(i + 1, int(it["k1"])) - int(it["k0"]))
+        cost.append(c)
+    cost = np.array(cost)
+    assert (np.diff(cost) <= 0).all(), "items must be heaviest first"
+    assert cost.sum() == int(h["visible_pairs"]) == 8192 * 8193 // 2
+    # no item carries more than 1/200 of the work, so 256 CUs stay busy
+    assert cost.max() * 200 < cost.sum()
+    assert int(h["num_items"]) >= 4 * 256
+
+
+def test_metadata_mismatch_rejected(lib):
+    p = _prob()
+    meta = B.li_metadata(p, B.make_lengths())
+    q = _prob(s2=65)
+    with pytest.raises(B.LIError) as e:
+        B.li_workspace_size(q, meta)
+    assert e.value.status == B.ERR_METADATA_MISMATCH
+    junk = np.zeros_like(meta)
+    with pytest.raises(B.LIError) as e:
+        B.li_workspace_size(p, junk)
+    assert e.value.status == B.ERR_METADATA_MISMATCH
+
+
+def test_compute_calls_validate_before_launch(lib):
+    """Error paths of li_score / li_topk / li_indexer return before any launch."""
+    p = _prob()
+    meta = B.li_metadata(p, B.make_lengths())
+    ws = B.li_workspace_size(p, meta)
+    fake = 1 << 20   # never dereferenced: every call below fails validation first
+    inp = B.make_inputs(fake, fake, 0)
+    with pytest.raises(B.LIError) as e:           # w missing
+        B.li_score(p, inp, meta, fake, fake, ws)
+    assert e.value.status == B.ERR_INVALID_ARGUMENT
+    inp = B.make_inputs(fake, fake, fake)
+    with pytest.raises(B.LIError) as e:           # workspace short
+        B.li_score(p, inp, meta, fake, fake, ws - 4)
+    assert e.value.status == B.ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(B.LIError) as e:           # no metadata on device
+        B.li_score(p, inp, meta, 0, fake, ws)
+    assert e.value.status == B.ERR_INVALID_ARGUMENT
+    pv = _prob(return_value=True)
+    metav = B.li_metadata(pv, B.make_lengths())
+    with pytest.raises(B.LIError) as e:           # values requested, no buffer
+        B.li_topk(pv, metav, fake, fake, ws, fake, 0)
+    assert e.value.status == B.ERR_INVALID_ARGUMENT
+    with pytest.raises(B.LIError) as e:
+        B.li_indexer(pv, inp, metav, fake, fake, ws, fake, 0)
+    assert e.value.status == B.ERR_INVALID_ARGUMENT
+    q8 = _prob(dtype_qk="e4m3fn")
+    meta8 = B.li_metadata(q8, B.make_lengths())
+    with pytest.raises(B.LIError) as e:           # quantised inputs need scales
+        B.li_score(q8, inp, meta8, fake, fake, B.li_workspace_size(q8, meta8))
+    assert e.value.status == B.ERR_INVALID_ARGUMENT
+    pa = _prob(layout_k="PA_BSND", block_size=16, num_blocks=16, max_blocks_per_seq=4)
+    metapa = B.li_metadata(pa, B.make_lengths(seqused_k=[64, 10]))
+    with pytest.raises(B.LIError) as e:           # paged keys need a block table
+        B.li_score(pa, inp, metapa, fake, fake, B.li_workspace_size(pa, metapa))
+    assert e.value.status == B.ERR_INVALID_ARGUMENT

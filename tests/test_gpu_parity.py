@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Small cases compare every row; the full-size workloads compare a sampled set
+of rows (first rows, rows around the point where n_valid crosses k, the last
+rows, and seeded random rows) in the launch configuration the benchmark uses.
+Acceptance per row is the rule in tests/checker.py.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import li_oracle as O
+from sparse_attention_top_amd import binding as B
+from sparse_attention_top_amd import indexer as I
+from sparse_attention_top_amd import synth
+from tests.checker import TOL, check_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _flat_rows(wl, arr):
+    """(B,S1,N2,k) or (T1,N2,k) -> (rows, N2, k) in oracle row order (all rows)."""
+    return arr.reshape(-1, wl.N2, wl.sparse_count)
+
+
+def _row_index(wl, rows):
+    return np.array([wl.row_of(b, i) for (b, i) in rows], dtype=np.int64)
+
+
+def run_and_check(wl, rows=None, return_value=True, label=""):
+    _say(f"[gpu] {label or wl.name}: rows={wl.num_rows} pairs={wl.visible_pairs()}")
+    idx, val, plan, _ = I.run_workload(wl, DEV, return_value=return_value)
+    torch.cuda.synchronize()
+    gi = _flat_rows(wl, idx.cpu().numpy())
+    gv = _flat_rows(wl, val.cpu().numpy()) if return_value else None
+    o = O.run(wl, rows=rows, want_scores=True)
+    sel = _row_index(wl, o["rows"])
+    st = check_rows(gi[sel], None if gv is None else gv[sel], o, wl.sparse_count,
+                    TOL[wl.qk_dtype], label=label or wl.name)
+    if rows is None:   # rows the oracle did not visit must not exist
+        assert sel.shape[0] == gi.shape[0]
+    _say(f"[gpu] {label or wl.name}: {st}")
+    return st, idx, val
+
+
+# ---------------------------------------------------------------------------
+# small cases: every row
+# ---------------------------------------------------------------------------
+def test_tiny_bsnd_config_all_rows():
+    run_and_check(synth.tiny_bsnd(), label="tiny_bsnd")
+
+
+SMALL = {
+    "test_shape_small": lambda: synth.test_shape(S1=96, S2=700, sparse_count=128),
+    "prefill_small": lambda: synth.dsa_prefill(S=600, sparse_count=256),
+    "paged_small": lambda: synth.paged_decode(B=5, lo=300, hi=3000, sparse_count=256),
+    "paged_bs16": lambda: synth.paged_decode(B=3, lo=100, hi=700, block_size=16,
+                                             sparse_count=64),
+    "paged_bs1024": lambda: synth.paged_decode(B=2, lo=1500, hi=2600, block_size=1024,
+                                               sparse_count=300),
+    "quant_fp8_small": lambda: synth.quant_varlen_tnd(nseq=4, lo=50, hi=700, sparse_count=128),
+    "quant_i8_small": lambda: synth.quant_varlen_tnd(nseq=3, lo=40, hi=500, qk_dtype="i8",
+                                                     sparse_count=96),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_configs_all_rows(name):
+    run_and_check(SMALL[name](), label=name)
+
+
+EDGE = {
+    # more queries than keys: the first rows see nothing
+    "sq_gt_sk": dict(layout_q="BSND", layout_k="BSND", qk_dtype="bf16", w_dtype="bf16", N1=64,
+                     D=128, seqlens_q=[90], seqlens_k=[40], sparse_count=16, sparse_mode=3),
+    # padding rows past seqused_q, poisoned keys past seqused_k, an empty sequence
+    "seqused": dict(layout_q="BSND", layout_k="BSND", qk_dtype="f16", w_dtype="f32", N1=24,
+                    D=128, seqlens_q=[33, 70, 0], seqlens_k=[200, 64, 10], S1=70, S2=250,
+                    sparse_count=48, sparse_mode=3),
+    "nomask_seqused_k": dict(layout_q="BSND", layout_k="BSND", qk_dtype="bf16", w_dtype="f32",
+                             N1=40, D=64, seqlens_q=[20, 20], seqlens_k=[333, 97], S2=400,
+                             sparse_count=64, sparse_mode=0),
+    # varlen with empty sequences in the middle and at the end
+    "tnd_empty": dict(layout_q="TND", layout_k="TND", qk_dtype="bf16", w_dtype="bf16", N1=64,
+                      D=128, seqlens_q=[17, 0, 130, 1, 0], seqlens_k=[17, 0, 130, 1, 0],
+                      sparse_count=32, sparse_mode=3),
+    "k1": dict(layout_q="BSND", layout_k="BSND", qk_dtype="bf16", w_dtype="bf16", N1=64, D=128,
+               seqlens_q=[70], seqlens_k=[300], sparse_count=1, sparse_mode=3),
+    "k2048_short_rows": dict(layout_q="BSND", layout_k="BSND", qk_dtype="f16", w_dtype="f16",
+                             N1=8, D=128, seqlens_q=[40], seqlens_k=[700], sparse_count=2048,
+                             sparse_mode=3),
+    "k2048_select": dict(layout_q="BSND", layout_k="BSND", qk_dtype="bf16", w_dtype="bf16",
+                         N1=16, D=64, seqlens_q=[9], seqlens_k=[5000], sparse_count=2048,
+                         sparse_mode=0),
+    "fp8_d64": dict(layout_q="TND", layout_k="TND", qk_dtype="e4m3fn", w_dtype="f32", N1=48,
+                    D=64, seqlens_q=[100, 260], seqlens_k=[100, 260], sparse_count=64,
+                    sparse_mode=3),
+    "i8_d64_bsnd": dict(layout_q="BSND", layout_k="BSND", qk_dtype="i8", w_dtype="f16", N1=64,
+                        D=64, seqlens_q=[50], seqlens_k=[400], sparse_count=100, sparse_mode=0),
+    "fp8_paged": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="e4m3fn", w_dtype="f32",
+                      N1=64, D=128, seqlens_q=[4, 4, 4], seqlens_k=[500, 129, 1000],
+                      sparse_count=128, sparse_mode=3, block_size=128),
+    "mid_variant": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16", w_dtype="bf16",
+                        N1=64, D=128, seqlens_q=[3, 4, 1], seqlens_k=[700, 40, 1200],
+                        sparse_count=100, sparse_mode=3, block_size=64),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases_all_rows(name):
+    wl = synth.build(name, seed=zlib.crc32(name.encode()), **EDGE[name])
+    run_and_check(wl, label=name)
+
+
+def _integer_workload(qk_dtype="bf16", mode=3, seed=5):
+    """Small-integer q/k and power-of-two weights: every score is exact in fp32,
+    so GPU and oracle must agree bit for bit, ties (lowest index first) included."""
+    rng = np.random.default_rng(seed)
+    wl = synth.build("int", layout_q="BSND", layout_k="BSND", qk_dtype=qk_dtype, w_dtype="f32",
+                     N1=64, D=128, seqlens_q=[150], seqlens_k=[400], sparse_count=96,
+                     sparse_mode=mode, seed=seed)
+    q = rng.integers(-2, 3, wl.q.shape).astype(np.float32)
+    k = rng.integers(-2, 3, wl.k.shape).astype(np.float32)
+    if qk_dtype == "bf16":
+        wl.q, wl.k = synth.encode_bf16(q), synth.encode_bf16(k)
+    else:
+        wl.q, wl.k = synth.encode_f16(q), synth.encode_f16(k)
+    wl.w = (rng.integers(-4, 5, wl.w.shape) / 8.0).astype(np.float32)
+    return wl
+
+
+@pytest.mark.parametrize("dt,mode", [("bf16", 3), ("f16", 0)])
+def test_integer_inputs_bit_exact(dt, mode):
+    wl = _integer_workload(dt, mode)
+    idx, val, _, _ = I.run_workload(wl, DEV, return_value=True)
+    oi, ov = O.run_full(wl)
+    gi, gv = idx.cpu().numpy(), val.cpu().numpy()
+    assert np.array_equal(gi, oi), "indices differ from the oracle on exact inputs"
+    assert np.array_equal(gv, ov), "values differ from the oracle on exact inputs"
+
+
+def test_zero_weights_give_lowest_indices():
+    """All scores are 0: the top-k is keys 0..m-1 in index order, values 0."""
+    wl = synth.build("zero", layout_q="BSND", layout_k="BSND", qk_dtype="bf16", w_dtype="f32",
+                     N1=64, D=128, seqlens_q=[64], seqlens_k=[3000], sparse_count=700,
+                     sparse_mode=3, seed=9)
+    wl.w = np.zeros_like(wl.w)
+    idx, val, _, _ = I.run_workload(wl, DEV, return_value=True)
+    gi = idx.cpu().numpy().reshape(64, 700)
+    gv = val.cpu().numpy().reshape(64, 700)
+    for i in range(64):
+        n = 3000 - 64 + i + 1
+        m = min(n, 700)
+        assert gi[i, :m].tolist() == list(range(m))
+        assert (gv[i, :m] == 0).all() and not np.signbit(gv[i, :m]).any()
+
+
+def test_deterministic_bitwise():
+    wl = synth.dsa_prefill(S=1000, sparse_count=256)
+    i1, v1, _, _ = I.run_workload(wl, DEV, return_value=True)
+    i2, v2, _, _ = I.run_workload(wl, DEV, return_value=True)
+    assert torch.equal(i1, i2) and torch.equal(v1, v2)
+
+
+def test_values_flag_does_not_change_indices():
+    wl = synth.test_shape(S1=64, S2=900, sparse_count=200)
+    i1, _, _, _ = I.run_workload(wl, DEV, return_value=False)
+    i2, _, _, _ = I.run_workload(wl, DEV, return_value=True)
+    assert torch.equal(i1, i2)
+
+
+def test_torch_api_matches_workload_path():
+    """The MindSpore-style torch entry point gives what the raw C-ABI path gives."""
+    wl = synth.quant_varlen_tnd(nseq=3, lo=30, hi=300, sparse_count=64)
+    i1, v1, _, dw = I.run_workload(wl, DEV, return_value=True)
+    i2, v2 = I.lightning_indexer(dw.q, dw.k, dw.w, sparse_count=64,
+                                 actual_seq_lengths_query=wl.cu_seqlens_q[1:],
+                                 actual_seq_lengths_key=wl.cu_seqlens_k[1:],
+                                 layout_query="TND", layout_key="TND", sparse_mode=3,
+                                 return_value=True, query_dequant_scale=dw.q_scale,
+                                 key_dequant_scale=dw.k_scale)
+    assert torch.equal(i1, i2) and torch.equal(v1, v2)
+    pa = synth.paged_decode(B=3, lo=200, hi=900, sparse_count=50)
+    i1, _, _, dw = I.run_workload(pa, DEV, return_value=False)
+    i2, v2 = I.lightning_indexer(dw.q, dw.k, dw.w, sparse_count=50,
+                                 actual_seq_lengths_key=pa.seqused_k, block_table=dw.block_table,
+                                 layout_query="BSND", layout_key="PA_BSND", sparse_mode=3)
+    assert torch.equal(i1, i2) and v2.shape == (0,)
+
+
+def test_strided_paged_cache():
+    """The paged cache's block axis may be strided (the quant README's stride attribute)."""
+    pa = synth.paged_decode(B=3, lo=200, hi=900, block_size=32, sparse_count=40)
+    i1, _, _, dw = I.run_workload(pa, DEV, return_value=False)
+    nb = dw.k.shape[0]
+    big = torch.zeros((nb, 2) + tuple(dw.k.shape[1:]), dtype=dw.k.dtype, device=DEV)
+    big[:, 1] = dw.k
+    strided = big[:, 1]
+    assert not strided.is_contiguous()
+    i2, _ = I.lightning_indexer(dw.q, strided, dw.w, sparse_count=40,
+                                actual_seq_lengths_key=pa.seqused_k, block_table=dw.block_table,
+                                layout_query="BSND", layout_key="PA_BSND", sparse_mode=3)
+    assert torch.equal(i1, i2)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled rows
+# ---------------------------------------------------------------------------
+def _sample_rows(wl, n_random=24, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(wl.B):
+        sq = int(wl.seqlens_q[b])
+        if sq == 0:
+            continue
+        cand = {0, sq - 1, sq // 2}
+        for i in range(sq):                       # where n_valid crosses k
+            if wl.n_valid(b, i) in (wl.sparse_count, wl.sparse_count + 1):
+                cand.add(i)
+        rows.update((b, i) for i in cand if 0 <= i < sq)
+    all_b = [b for b in range(wl.B) if wl.seqlens_q[b] > 0]
+    for _ in range(n_random):
+        b = int(rng.choice(all_b))
+        rows.add((b, int(rng.integers(0, int(wl.seqlens_q[b])))))
+    if len(rows) > 160:
+        rows = set(sorted(rows)[:: max(1, len(rows) // 160)])
+    return sorted(rows)
+
+
+FULL = {
+    "tiny_bsnd": synth.tiny_bsnd,
+    "test_shape": synth.test_shape,
+    "dsa_prefill": synth.dsa_prefill,
+    "paged_decode": synth.paged_decode,
+    "quant_varlen_tnd": synth.quant_varlen_tnd,
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled_rows(name):
+    wl = FULL[name]()
+    rows = _sample_rows(wl)
+    st, _, _ = run_and_check(wl, rows=rows, return_value=True, label=f"{name}[full]")
+    assert st.rows >= len(rows)
