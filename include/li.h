@@ -140,10 +140,12 @@ typedef struct li_problem {
  *                last == t1. Required for TND queries, rejected for BSND.
  *  cu_seqlens_k  (B+1) int32: same for TND keys. Required for TND keys,
  *                rejected for BSND and PA_BSND.
- *  seqused_q     (B) int32, BSND only, optional: actual query length <= s1 of each
- *                batch (rows past it are unused); NULL means s1.
- *  seqused_k     (B) int32: actual key lengths. Optional for BSND (<= s2, NULL
- *                means s2), required for PA_BSND, rejected for TND.
+ *  seqused_q     (B) int32, optional: actual query length of each batch, <= s1
+ *                (BSND) or <= the cu_seqlens_q length (TND); rows past it are
+ *                unused. NULL means the full length.
+ *  seqused_k     (B) int32: actual key lengths. Optional for BSND (<= s2) and
+ *                TND (<= the cu_seqlens_k length), NULL meaning the full length;
+ *                required for PA_BSND (covered by max_blocks_per_seq blocks).
  */
 typedef struct li_lengths {
   const int32_t* cu_seqlens_q;
@@ -158,6 +160,8 @@ typedef struct li_lengths {
  *  q_scale, k_scale  float32 dequant scales, required for E4M3FN / I8, else NULL.
  *  block_table   (B, max_blocks_per_seq) int32 physical block ids, required for
  *                PA_BSND; entries past a sequence's last block are never read.
+ *                Ids outside [0, num_blocks) are clamped into that range (no
+ *                fault; the scores of the keys they cover are then unspecified).
  */
 typedef struct li_inputs {
   const void* q;

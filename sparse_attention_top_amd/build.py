@@ -23,7 +23,10 @@ LIBNAME = "libli_mi355x.so"
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of the generated code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA accumulators in VGPRs (the epilogue reads them with VALU ops);
+                # operand fragments are placed in AGPRs by the kernels themselves.
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
                 "-Wall", "-Wno-unused-function"]
 

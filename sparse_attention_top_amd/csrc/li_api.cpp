@@ -270,11 +270,18 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     int64_t pairs = 0;
     for (int b = 0; b < B; ++b)
       for (int i = 0; i < sq[b]; ++i) pairs += visible_keys(i, sq[b], sk[b], p->sparse_mode);
-    const int64_t target_items = 8ll * num_cus;
-    int64_t chunk = (pairs + TQ * target_items - 1) / (TQ * target_items);
-    chunk = std::max<int64_t>(chunk, 8ll * KT);
-    chunk = (chunk + KT - 1) / KT * KT;
-    chunk = std::min<int64_t>(chunk, std::max<int64_t>(KT, ((int64_t)max_sk + KT - 1) / KT * KT));
+    // Each key chunk of a row tile re-reads the tile's query heads, so rows are
+    // split along keys only when there are too few row tiles to fill the CUs.
+    int64_t tiles = 0;
+    for (int b = 0; b < B; ++b) tiles += (sq[b] + TQ - 1) / TQ;
+    const int64_t whole = std::max<int64_t>(KT, ((int64_t)max_sk + KT - 1) / KT * KT);
+    int64_t chunk = whole;
+    if (tiles < 2ll * num_cus) {
+      const int64_t target_items = 4ll * num_cus;
+      chunk = (pairs + TQ * target_items - 1) / (TQ * target_items);
+      chunk = std::max<int64_t>(chunk, 8ll * KT);
+      chunk = std::min<int64_t>((chunk + KT - 1) / KT * KT, whole);
+    }
 
     // ---- sequences ----
     std::vector<BatchRec> recs(B);
@@ -405,6 +412,9 @@ li_status li_score(const li_problem* p, const li_inputs* in, const void* meta_ho
   a.layout_k = p->layout_k;
   a.dtype_w = p->dtype_w;
   a.block_size = p->block_size;
+  a.block_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if (p->block_size == (1 << sh)) a.block_shift = sh;
   a.max_blocks = p->max_blocks_per_seq;
   a.sparse_mode = p->sparse_mode;
   const hipError_t e = launch_score(*p, h->variant, h->num_items, a, (hipStream_t)stream);
@@ -437,6 +447,7 @@ li_status li_topk(const li_problem* p, const void* meta_host, const void* meta_d
   a.batch = p->batch;
   a.k = p->sparse_count;
   a.sparse_mode = p->sparse_mode;
+  a.max_keys = h->max_sk;
   const hipError_t e = launch_topk(*p, a, (hipStream_t)stream);
   LI_CHECK(e == hipSuccess, LI_ERR_HIP, "top-k kernel launch: %s", hipGetErrorString(e));
   return LI_OK;

@@ -59,15 +59,15 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == 16, "work item size");
 
-// Score-kernel variants: waves along query rows (WQ) x waves along keys (WK),
-// 8 waves per workgroup, KT keys staged in LDS per step.
+// Score-kernel variants: 8 waves of one query row each, arranged as WQ rows x
+// WK key slices; KT keys staged in LDS per step.
 enum ScoreVariant : int32_t {
   kVarPrefill = 0,  // WQ=8, WK=1: 8 query rows share each staged key tile
-  kVarMid = 1,      // WQ=4, WK=2
+  kVarMid = 1,      // WQ=4, WK=2: 4 query rows
   kVarDecode = 2,   // WQ=2, WK=4: 2 query rows, waves split the keys
 };
 constexpr int kVariantTileQ[3] = {8, 4, 2};
-constexpr int kVariantTileK[3] = {64, 128, 128};
+constexpr int kVariantTileK[3] = {128, 128, 128};
 
 // ---------------------------------------------------------------------------
 // Kernel arguments
@@ -83,11 +83,12 @@ struct ScoreArgs {
   const WorkItem* items;
   float* ws;
   int64_t k_block_stride;  // elements between paged blocks
-  int64_t num_blocks;      // paged blocks; ids outside [0, num_blocks) read as zero keys
+  int64_t num_blocks;      // paged blocks; ids outside [0, num_blocks) are clamped into it
   int32_t n1;              // query heads (== G since N2 == 1)
   int32_t layout_k;
   int32_t dtype_w;
   int32_t block_size;
+  int32_t block_shift;     // log2(block_size) when it is a power of two, else -1
   int32_t max_blocks;
   int32_t sparse_mode;
 };
@@ -101,6 +102,7 @@ struct TopkArgs {
   int32_t batch;
   int32_t k;
   int32_t sparse_mode;
+  int32_t max_keys;        // longest row (visible keys), picks the register tiling
 };
 
 // Host launchers (defined next to their kernels).
