@@ -67,7 +67,7 @@ enum ScoreVariant : int32_t {
   kVarDecode = 2,   // WQ=2, WK=4: 2 query rows, waves split the keys
 };
 constexpr int kVariantTileQ[3] = {8, 4, 2};
-constexpr int kVariantTileK[3] = {128, 128, 128};
+constexpr int kVariantTileK[3] = {128, 128, 256};
 
 // ---------------------------------------------------------------------------
 // Kernel arguments

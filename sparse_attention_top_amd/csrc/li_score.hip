@@ -23,6 +23,8 @@
 //     cross-lane swap-add over the two half-waves completes the reduction.
 #include "li_internal.h"
 
+#include <utility>
+
 namespace li {
 namespace {
 
@@ -114,6 +116,38 @@ __device__ inline float load_weight(const void* w, int dtype, int64_t i) {
   return (float)__builtin_bit_cast(_Float16, bits);
 }
 
+// Buffer resource word 3 for raw (untyped) buffer access on gfx9-family GPUs.
+// With a zero stride, a lane whose byte offset is >= the record count reads 0
+// and has its store dropped by the hardware: masked stores need no branch.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kDropOffset = (int)0x80000000u;
+
+template <int N, typename F, int... I>
+__device__ inline void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ inline void unroll(F&& f) {
+  unroll_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane i of the wave writes
+// LDS bytes [lds + 16 i, lds + 16 i + 16). The LDS base is wave-uniform (M0).
+// Issued from asm so that the compiler's own wait-count bookkeeping does not
+// treat the in-flight staging buffer as aliasing the one being read; the
+// completion wait is explicit (stage_barrier). No VGPR is written.
+__device__ inline void lds_dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(gptr)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and all its LDS operations are done, then barrier the workgroup.
+template <int N> __device__ inline void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
 template <int DT, int D, int NT, int WQ, int WK, int KT>
 __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
   using M = Mma<DT>;
@@ -123,26 +157,34 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
   constexpr int LB = M::kLaneBytes;
   constexpr int ROW = D * ES;              // bytes of one key row
   constexpr int KSTEPS = ROW / (2 * LB);   // MFMA k-steps over the head dim
-  constexpr int ROWP = ROW + 16;           // LDS row pitch (16-byte pad vs bank conflicts)
-  constexpr int NTHR = WQ * WK * 64;
-  constexpr int CPR = ROW / 16;            // 16-byte chunks per key row
-  constexpr int NCHUNK = KT * CPR;
-  constexpr int CPT = (NCHUNK + NTHR - 1) / NTHR;
+  constexpr int NW = WQ * WK;              // waves
+  constexpr int NTHR = NW * 64;
+  constexpr int STAGE = KT * ROW;          // bytes of one staged key tile
+  constexpr int DMA = STAGE / 1024;        // 1 KB wave loads per stage
+  constexpr int DPW = DMA / NW;            // ... per wave
+  constexpr int U = ROW / LB;              // swizzle units per key row
+  constexpr int RPW = ROW >= 128 ? 1 : 128 / ROW;   // key rows per 128-byte bank window
   constexpr bool QUANT = (DT == LI_DTYPE_E4M3FN) || (DT == LI_DTYPE_I8);
   constexpr int SPS = KT / 32 / WK;        // 32-key slices per staged tile per wave
   constexpr int EPM = 16 / KSTEPS;         // previous-slice accumulators per MFMA
-  static_assert(KT % (32 * WK) == 0, "key tile must split into 32-key slices");
+  static_assert(KT % (32 * WK) == 0 && SPS % 2 == 0, "a stage holds an even number of slices");
   static_assert(KSTEPS >= 1 && ROW % (2 * LB) == 0, "head dim must fill whole k-steps");
+  static_assert(STAGE % (1024 * NW) == 0, "every wave stages the same number of 1 KB blocks");
+  static_assert((ROW & (ROW - 1)) == 0 && (U & (U - 1)) == 0, "power-of-two rows");
   static_assert(!QUANT || KT <= NTHR, "one thread per staged key scale");
 
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KT * ROWP];
+  // Two staged key tiles. Key row r of a tile occupies bytes [r*ROW, (r+1)*ROW);
+  // its LB-byte unit u is stored at unit position u ^ swz(r), so that the 32
+  // rows read together by a B-fragment load spread over all LDS banks.
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2 * STAGE];
   __shared__ float ksc[2][QUANT ? KT : 1];
+  auto swz = [](int r) { return (r / RPW) & (U - 1); };
 
   const WorkItem it = a.items[blockIdx.x];
   const BatchRec br = a.batches[it.b];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wq = wave % WQ;
   const int wk = wave / WQ;
   const int half = lane >> 5;
@@ -154,157 +196,192 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
   const int lim = nv < it.k1 ? nv : it.k1;   // this row stores keys [k0, lim)
   const int64_t qrow = (int64_t)br.row_base + (row_ok ? row : 0);
   float* out_row = a.ws + br.ws_off + (int64_t)(row_ok ? row : 0) * br.ld;
+  const auto out_rsrc = __builtin_amdgcn_make_buffer_rsrc(out_row, (short)0, lim > 0 ? lim * 4 : 0,
+                                                          kRsrcWord3);
+
+  // Key staging. Stage st covers keys [k0 + st*KT, k0 + (st+1)*KT); keys past
+  // k1 are clamped to the item's last key (computed, never stored), so every
+  // load is unconditional. For the paged cache the block ids of a stage are
+  // loaded one stage before its keys.
+  const bool paged = a.layout_k == LI_LAYOUT_PA_BSND;
+  const int jmax = it.k1 - 1;
+  const int32_t* btab = a.block_table + (int64_t)it.b * a.max_blocks;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)kbuf;
+  // LDS byte (of the wave's d-th 1 KB block) this lane writes, and the key row
+  // and byte within the row that belong there.
+  auto dma_row = [&](int d) { return ((d * NW + wave) * 1024 + lane * 16) / ROW; };
+  auto dma_byte = [&](int d) {
+    const int r = dma_row(d);
+    const int b = (lane * 16) % ROW;   // 1 KB blocks hold whole rows
+    return (((b / LB) ^ swz(r)) * LB) + (b % LB);
+  };
+  auto stage_key = [&](int st, int kk) { return min(it.k0 + st * KT + kk, jmax); };
+  auto block_index = [&](int j) { return a.block_shift >= 0 ? j >> a.block_shift : j / a.block_size; };
+  auto clamp_block = [&](int blk) {
+    return blk < 0 ? 0 : (blk >= a.num_blocks ? (int)(a.num_blocks - 1) : blk);
+  };
+  int pid[DPW];
+  int psid = 0;
+  auto ids = [&](int st) {
+    if (!paged) return;
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) pid[d] = btab[block_index(stage_key(st, dma_row(d)))];
+    if (QUANT) psid = btab[block_index(stage_key(st, tid % KT))];
+  };
+  float pre_sc = 0.f;
+  auto fetch = [&](int st) {
+    const uint32_t lds = lds0 + (st & 1) * STAGE;
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int j = stage_key(st, dma_row(d));
+      int64_t off;
+      if (paged) {
+        const int bo = j - block_index(j) * a.block_size;
+        off = ((int64_t)clamp_block(pid[d]) * a.k_block_stride + (int64_t)bo * D) * ES;
+      } else {
+        off = ((int64_t)br.k_base + j) * ROW;
+      }
+      lds_dma16(a.k + off + dma_byte(d), lds + (d * NW + wave) * 1024);
+    }
+    if (QUANT) {
+      const int j = stage_key(st, tid % KT);
+      const int64_t off = paged ? (int64_t)clamp_block(psid) * a.block_size + (j - block_index(j) * a.block_size)
+                                : (int64_t)br.k_base + j;
+      pre_sc = a.k_scale[off];
+    }
+  };
+  auto stash_scales = [&](int st) {
+    if (QUANT && tid < KT) ksc[st & 1][tid] = pre_sc;
+  };
+
+  const int nstages = (it.k1 - it.k0 + KT - 1) / KT;
+  ids(0);
+  fetch(0);
+  stash_scales(0);
+  if (nstages > 1) {
+    ids(1);
+    fetch(1);
+  }
+  if (nstages > 2) ids(2);
 
   // Query heads of this row as MFMA A-operands (zero for padded heads), and the
-  // per-lane weights of the 16 heads each lane accumulates per tile.
+  // per-lane weights of the 16 heads each lane accumulates per tile. Every load
+  // is unconditional (clamped index, masked afterwards) so that they are all in
+  // flight together with the first key tiles.
   Frag qf[NT][KSTEPS];
-  float wr[NT][16];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int h = 32 * t + col;
     const bool ok = row_ok && h < a.n1;
     const uint8_t* src = a.q + ((qrow * a.n1 + (ok ? h : 0)) * D) * ES + half * LB;
+    const int mask = ok ? -1 : 0;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[t][s] = ok ? load_frag<Frag>(src + s * 2 * LB) : Frag{};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int he = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-      float v = 0.f;
-      if (row_ok && he < a.n1) {
-        v = load_weight(a.w, a.dtype_w, qrow * a.n1 + he);
-        if (QUANT) v *= a.q_scale[qrow * a.n1 + he];
-      }
-      wr[t][e] = v;
-    }
+    for (int s = 0; s < KSTEPS; ++s) qf[t][s] = load_frag<Frag>(src + s * 2 * LB) & mask;
   }
-
-  // Global -> register prefetch of one key stage. Keys past k1 are clamped to
-  // the last key of the item: their columns are computed but never stored, so
-  // every load is unconditional (no per-lane branches, no zero fill).
-  i32x4_t pre[CPT];
-  float pre_sc = 0.f;
-  const bool paged = a.layout_k == LI_LAYOUT_PA_BSND;
-  const int jmax = it.k1 - 1;
-  auto key_off = [&](int j) -> int64_t {   // element offset of key j's row
-    if (paged) {
-      int bi, bo;
-      if (a.block_shift >= 0) {
-        bi = j >> a.block_shift;
-        bo = j & (a.block_size - 1);
-      } else {
-        bi = j / a.block_size;
-        bo = j - bi * a.block_size;
-      }
-      int blk = a.block_table[(int64_t)it.b * a.max_blocks + bi];
-      blk = blk < 0 ? 0 : (blk >= a.num_blocks ? (int)(a.num_blocks - 1) : blk);
-      return (int64_t)blk * a.k_block_stride + (int64_t)bo * D;
-    }
-    return ((int64_t)br.k_base + j) * D;
-  };
-  auto scale_off = [&](int j) -> int64_t { // offset of key j's dequant scale
-    if (paged) {
-      int bi, bo;
-      if (a.block_shift >= 0) {
-        bi = j >> a.block_shift;
-        bo = j & (a.block_size - 1);
-      } else {
-        bi = j / a.block_size;
-        bo = j - bi * a.block_size;
-      }
-      int blk = a.block_table[(int64_t)it.b * a.max_blocks + bi];
-      blk = blk < 0 ? 0 : (blk >= a.num_blocks ? (int)(a.num_blocks - 1) : blk);
-      return (int64_t)blk * a.block_size + bo;
-    }
-    return (int64_t)br.k_base + j;
-  };
-  auto fetch = [&](int ks0) {
+  float wr[NT][16];
+  {
+    int64_t widx[NT][16];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = (tid + c * NTHR) % NCHUNK;   // NCHUNK < NTHR re-reads a chunk
-      const int kk = ch / CPR;
-      const int cc = ch - kk * CPR;
-      const int j = min(ks0 + kk, jmax);
-      pre[c] = *reinterpret_cast<const i32x4_t*>(a.k + key_off(j) * ES + cc * 16);
-    }
-    if (QUANT && tid < KT) pre_sc = a.k_scale[scale_off(min(ks0 + tid, jmax))];
-  };
-  auto stash = [&](int buf) {
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NTHR;
-      if (ch < NCHUNK) {
-        const int kk = ch / CPR;
-        const int cc = ch - kk * CPR;
-        *reinterpret_cast<i32x4_t*>(&kbuf[buf][kk * ROWP + cc * 16]) = pre[c];
+      for (int e = 0; e < 16; ++e) {
+        const int he = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+        widx[t][e] = qrow * a.n1 + (he < a.n1 ? he : a.n1 - 1);
       }
+    if (a.dtype_w == LI_DTYPE_F32) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) wr[t][e] = static_cast<const float*>(a.w)[widx[t][e]];
+    } else {
+      uint16_t raw[NT][16];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) raw[t][e] = static_cast<const uint16_t*>(a.w)[widx[t][e]];
+      const bool is_bf16 = a.dtype_w == LI_DTYPE_BF16;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          wr[t][e] = is_bf16 ? __uint_as_float(uint32_t(raw[t][e]) << 16)
+                             : (float)__builtin_bit_cast(_Float16, raw[t][e]);
     }
-    if (QUANT && tid < KT) ksc[buf][tid] = pre_sc;
-  };
+    if (QUANT) {
+      float qs[NT][16];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qs[t][e] = a.q_scale[widx[t][e]];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) wr[t][e] *= qs[t][e];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int he = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+        wr[t][e] = (row_ok && he < a.n1) ? wr[t][e] : 0.f;
+      }
+  }
+  stage_barrier<0>();   // stage 0 (and 1) staged, query and weights in registers
 
-  // Flat loop over this wave's 32-key slices. Every wave runs every slice of the
-  // item (keys past a row's limit are computed but not stored), so barriers are
-  // uniform. Slice g:
-  //   * if g is the last slice of its staged tile: stash the next tile, barrier,
-  //     start fetching the tile after it (so slice g+1's fragments can be read);
-  //   * MFMAs of slice g; right after each k-step's MFMAs, that k-step's B
-  //     fragment register is reloaded with slice g+1's (LDS latency hidden by a
-  //     whole slice); the ReLU / weight / in-lane head reduction of slice g-1 is
-  //     interleaved between the MFMAs;
-  //   * cross-half swap-add and store of slice g-1.
-  const int nstages = (it.k1 - it.k0 + KT - 1) / KT;
-  const int nslices = nstages * SPS;
-  fetch(it.k0);
-  stash(0);
-  __syncthreads();
-  if (nstages > 1) fetch(it.k0 + KT);
-
-  auto slice_loc = [&](int g, int& buf, int& sub) {
-    const int st = g / SPS;
-    sub = wk + (g - st * SPS) * WK;
-    buf = st & 1;
-    return it.k0 + st * KT + sub * 32;
+  // One loop iteration per stage, its SPS slices unrolled. Slice i of stage st
+  // covers keys [k0 + st*KT + (wk + i*WK)*32, +32) in buffer st & 1. Before the
+  // last slice of a stage every wave has read all it needs of that buffer, so
+  // after a barrier (which also publishes the next stage, loaded a stage
+  // earlier) the stage after next is loaded into it. Per slice: MFMAs of the
+  // slice, each k-step's B fragment reloaded right after use with the next
+  // slice's, and the ReLU / weight / in-lane head reduction of the previous
+  // slice interleaved between the MFMAs; then the cross-half swap-add and the
+  // store of that previous slice. The store has no branch, so the last SPS
+  // vector-memory operations before each barrier are exactly SPS stores.
+  auto slice_key = [&](int st, int i) { return it.k0 + st * KT + (wk + i * WK) * 32; };
+  // LDS byte address of this lane's B fragment of k-step s in slice (buf, sub):
+  // frag_base(buf, sub) ^ (2*LB*s), rows being ROW-aligned.
+  auto frag_base = [&](int buf, int sub) {
+    const int r = sub * 32 + col;
+    const int x = swz(r);
+    return buf * STAGE + r * ROW + LB * (half ^ (x & 1)) + 2 * LB * (x >> 1);
   };
-  auto boundary = [&](int g) {
-    if ((g + 1) % SPS != 0) return;
-    const int st = g / SPS;
-    if (st + 1 < nstages) stash((st + 1) & 1);
-    __syncthreads();
-    if (st + 2 < nstages) fetch(it.k0 + (st + 2) * KT);
+  auto read_frag = [&](int base, int s) {
+    return *reinterpret_cast<const Frag*>(&kbuf[base ^ (2 * LB * s)]);
   };
   Frag bf[KSTEPS];
   {
-    int buf, sub;
-    slice_loc(0, buf, sub);
-    const uint8_t* bsrc = &kbuf[buf][(sub * 32 + col) * ROWP + half * LB];
+    const int b0 = frag_base(0, wk);
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) bf[s] = load_frag<Frag>(bsrc + s * 2 * LB);
+    for (int s = 0; s < KSTEPS; ++s) bf[s] = read_frag(b0, s);
   }
-  auto step = [&](int g, Acc (&acc)[NT], const Acc (&old)[NT], bool have_old, float& ks) {
-    int buf, sub;
-    slice_loc(g, buf, sub);
-    ks = QUANT ? ksc[buf][sub * 32 + col] : 1.f;
-    // Next slice's fragments (past the last slice: re-read this one, unused);
-    // unconditional so that the MFMA / VALU block stays one basic block.
-    int nbuf = buf, nsub = sub;
-    if (g + 1 < nslices) slice_loc(g + 1, nbuf, nsub);
-    const uint8_t* nsrc = &kbuf[nbuf][(nsub * 32 + col) * ROWP + half * LB];
+  // Dequant key scale of the next slice, read together with its B fragments.
+  float ksn = QUANT ? ksc[0][wk * 32 + col] : 1.f;
+  auto step = [&](int st, auto ic, Acc (&acc)[NT], const Acc (&old)[NT], float& ks) {
+    constexpr int i = decltype(ic)::value;
+    const int buf = st & 1;
+    ks = ksn;
+    // Next slice: same stage, or the first slice of the next stage (past the
+    // last stage this re-reads stale LDS, unused).
+    const int nbuf = (i + 1 < SPS) ? buf : (buf ^ 1);
+    const int nsub = (i + 1 < SPS) ? wk + (i + 1) * WK : wk;
+    const int nbase = frag_base(nbuf, nsub);
+    if (QUANT) ksn = ksc[nbuf][nsub * 32 + col];
     float p0 = 0.f, p1 = 0.f;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         acc[t] = M::mma(qf[t][s], bf[s], s == 0 ? M::zero() : acc[t]);
-        if (have_old) {
 #pragma unroll
-          for (int u = 0; u < EPM; u += 2) {
-            const int e = s * EPM + u;
-            p0 = fmaf(wr[t][e], M::relu(old[t], e), p0);
-            p1 = fmaf(wr[t][e + 1], M::relu(old[t], e + 1), p1);
-          }
+        for (int u = 0; u < EPM; u += 2) {
+          const int e = s * EPM + u;
+          p0 = fmaf(wr[t][e], M::relu(old[t], e), p0);
+          p1 = fmaf(wr[t][e + 1], M::relu(old[t], e + 1), p1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      bf[s] = load_frag<Frag>(nsrc + s * 2 * LB);
+      bf[s] = read_frag(nbase, s);
     }
     return p0 + p1;
   };
@@ -321,53 +398,57 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
     return p0 + p1;
   };
   // Cross-half swap-add (both halves end up with the full sum over heads) and
-  // the store of the slice starting at key kb.
-  auto finish = [&](float part, int kb, float ks) {
+  // the store of the slice starting at key kb by the lower half-wave; keys at
+  // or past the row's limit fall outside the buffer record and are dropped.
+  auto finish = [&](float part, int kb, float ks, bool valid) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
                                                      __float_as_uint(part), false, false);
     const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int j = kb + col;
-    if (half == 0 && j < lim) out_row[j] = QUANT ? tot * ks : tot;
-  };
-  auto key_of = [&](int g) {
-    int buf, sub;
-    return slice_loc(g, buf, sub);
+    const int off = (half == 0 && valid) ? (kb + col) * 4 : kDropOffset;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(QUANT ? tot * ks : tot), out_rsrc, off, 0, 0);
   };
 
-  Acc accA[NT], accB[NT];
-  float ksA = 1.f, ksB = 1.f;
-  boundary(0);
-  step(0, accA, accB, false, ksA);
-  int g = 1;
-  for (; g + 1 < nslices; g += 2) {
-    boundary(g);
-    float part = step(g, accB, accA, true, ksB);
-    finish(part, key_of(g - 1), ksA);
-    boundary(g + 1);
-    part = step(g + 1, accA, accB, true, ksA);
-    finish(part, key_of(g), ksB);
+  Acc acc0[NT], acc1[NT];   // even slices of a stage accumulate in acc0, odd in acc1
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc1[t] = M::zero();   // read by slice 0's (dropped) epilogue
+  float ks0 = 1.f, ks1 = 1.f;
+  for (int st = 0; st < nstages; ++st) {
+    unroll<SPS>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (i == SPS - 1) {
+        stash_scales(st + 1);   // scales of stage st+1 (ignored past the last stage)
+        stage_barrier<SPS>();
+        if (st + 2 < nstages) fetch(st + 2);
+        if (st + 3 < nstages) ids(st + 3);
+      }
+      // previous slice: (st, i-1), or the last slice of stage st-1
+      const int pkb = i > 0 ? slice_key(st, i - 1) : slice_key(st - 1, SPS - 1);
+      if (i % 2 == 0) {
+        const float part = step(st, ic, acc0, acc1, ks0);
+        finish(part, pkb, ks1, i > 0 || st > 0);
+      } else {
+        const float part = step(st, ic, acc1, acc0, ks1);
+        finish(part, pkb, ks0, true);
+      }
+    });
   }
-  if (g < nslices) {            // slice g computes into B, slice g-1 (A) drains
-    boundary(g);
-    const float part = step(g, accB, accA, true, ksB);
-    finish(part, key_of(g - 1), ksA);
-    finish(epi(accB), key_of(g), ksB);
-  } else {
-    finish(epi(accA), key_of(g - 1), ksA);
-  }
+  finish(epi(acc1), slice_key(nstages - 1, SPS - 1), ks1, true);
 }
 
 template <int DT, int D, int NT>
 hipError_t launch_v(int variant, int num_items, const ScoreArgs& a, hipStream_t s) {
   switch (variant) {
     case kVarPrefill:
-      hipLaunchKernelGGL((score_kernel<DT, D, NT, 8, 1, 128>), dim3(num_items), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((score_kernel<DT, D, NT, 8, 1, kVariantTileK[kVarPrefill]>), dim3(num_items),
+                         dim3(512), 0, s, a);
       break;
     case kVarMid:
-      hipLaunchKernelGGL((score_kernel<DT, D, NT, 4, 2, 128>), dim3(num_items), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((score_kernel<DT, D, NT, 4, 2, kVariantTileK[kVarMid]>), dim3(num_items),
+                         dim3(512), 0, s, a);
       break;
     case kVarDecode:
-      hipLaunchKernelGGL((score_kernel<DT, D, NT, 2, 4, 128>), dim3(num_items), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((score_kernel<DT, D, NT, 2, 4, kVariantTileK[kVarDecode]>), dim3(num_items),
+                         dim3(512), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;

@@ -111,6 +111,18 @@ EDGE = {
     "mid_variant": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16", w_dtype="bf16",
                         N1=64, D=128, seqlens_q=[3, 4, 1], seqlens_k=[700, 40, 1200],
                         sparse_count=100, sparse_mode=3, block_size=64),
+    # decode-shaped quantised rows: two query rows per sequence, long key ranges
+    "fp8_decode_tnd": dict(layout_q="TND", layout_k="TND", qk_dtype="e4m3fn", w_dtype="f32",
+                           N1=64, D=128, seqlens_q=[2, 1, 2], seqlens_k=[900, 300, 2000],
+                           sparse_count=256, sparse_mode=3),
+    # several cache blocks per staged key tile
+    "i8_paged_bs16": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="i8", w_dtype="bf16",
+                          N1=32, D=128, seqlens_q=[1, 2], seqlens_k=[500, 1700],
+                          sparse_count=200, sparse_mode=3, block_size=16),
+    # block size that is not a power of two (division path of the block lookup)
+    "paged_bs48": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16", w_dtype="f32",
+                       N1=64, D=128, seqlens_q=[5, 7], seqlens_k=[300, 1000],
+                       sparse_count=128, sparse_mode=3, block_size=48),
 }
 
 
