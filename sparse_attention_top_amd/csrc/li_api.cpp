@@ -323,9 +323,30 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
                      [](const Cand& x, const Cand& y) { return x.cost > y.cost; });
     LI_CHECK(cands.size() < ((size_t)1 << 31), LI_ERR_UNSUPPORTED, "too many work items");
 
+    // ---- top-k row table: rows grouped by size class, longest first ----
+    const int64_t nrows = num_rows(*p);
+    LI_CHECK(nrows < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED, "too many output rows");
+    struct RowCand {
+      RowRec r;
+      int32_t n;
+    };
+    std::vector<std::vector<RowCand>> by_class(kTopkClasses);
+    int64_t covered = 0;
+    for (int b = 0; b < B; ++b) {
+      for (int i = 0; i < rows[b]; ++i) {
+        const int n = i < sq[b] ? visible_keys(i, sq[b], sk[b], p->sparse_mode) : 0;
+        by_class[topk_class(n)].push_back({{(int32_t)(row_base[b] + i), b}, n});
+      }
+      covered += rows[b];
+    }
+    LI_CHECK(covered == nrows, LI_ERR_INVALID_ARGUMENT,
+             "sequences cover %lld output rows, the problem has %lld", (long long)covered,
+             (long long)nrows);
+
     const size_t off_b = sizeof(MetaHeader);
     const size_t off_i = off_b + sizeof(BatchRec) * (size_t)B;
-    const size_t need = off_i + sizeof(WorkItem) * cands.size();
+    const size_t off_r = off_i + sizeof(WorkItem) * cands.size();
+    const size_t need = off_r + sizeof(RowRec) * (size_t)nrows;
     *meta_bytes = need;
     if (meta_host == nullptr) return LI_OK;
     LI_CHECK(meta_capacity >= need, LI_ERR_BUFFER_TOO_SMALL,
@@ -349,11 +370,22 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     h.off_items = off_i;
     h.max_sk = max_sk;
     h.max_sq = max_sq;
+    h.off_rows = off_r;
     uint8_t* dst = static_cast<uint8_t*>(meta_host);
-    std::memcpy(dst, &h, sizeof h);
     std::memcpy(dst + off_b, recs.data(), sizeof(BatchRec) * (size_t)B);
     WorkItem* items = reinterpret_cast<WorkItem*>(dst + off_i);
     for (size_t n = 0; n < cands.size(); ++n) items[n] = cands[n].w;
+    RowRec* rrecs = reinterpret_cast<RowRec*>(dst + off_r);
+    int32_t pos = 0;
+    for (int c = 0; c < kTopkClasses; ++c) {
+      auto& v = by_class[c];
+      std::stable_sort(v.begin(), v.end(),
+                       [](const RowCand& x, const RowCand& y) { return x.n > y.n; });
+      h.row_class[c] = pos;
+      for (const RowCand& rc : v) rrecs[pos++] = rc.r;
+    }
+    h.row_class[kTopkClasses] = pos;
+    std::memcpy(dst, &h, sizeof h);
     return LI_OK;
   } catch (const std::exception& e) {
     return fail(LI_ERR_INVALID_ARGUMENT, "li_metadata: %s", e.what());
@@ -394,6 +426,7 @@ li_status li_score(const li_problem* p, const li_inputs* in, const void* meta_ho
            ws_bytes, need);
   LI_CHECK(((uintptr_t)in->q % 16) == 0 && ((uintptr_t)in->k % 16) == 0, LI_ERR_INVALID_ARGUMENT,
            "q and k must be 16-byte aligned");
+  LI_CHECK(((uintptr_t)ws % 16) == 0, LI_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
 
   ScoreArgs a;
   a.q = static_cast<const uint8_t*>(in->q);
@@ -438,16 +471,16 @@ li_status li_topk(const li_problem* p, const void* meta_host, const void* meta_d
   LI_CHECK(sparse_indices != nullptr, LI_ERR_INVALID_ARGUMENT, "sparse_indices is NULL");
   LI_CHECK(!p->return_value || sparse_values != nullptr, LI_ERR_INVALID_ARGUMENT,
            "return_value needs sparse_values");
+  LI_CHECK(((uintptr_t)ws % 16) == 0, LI_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   TopkArgs a;
   a.ws = static_cast<const float*>(ws);
   a.batches = meta_ptr<BatchRec>(meta_dev, h->off_batches);
+  a.rows = meta_ptr<RowRec>(meta_dev, h->off_rows);
   a.out_idx = sparse_indices;
   a.out_val = p->return_value ? sparse_values : nullptr;
-  a.num_rows = h->num_rows;
-  a.batch = p->batch;
   a.k = p->sparse_count;
   a.sparse_mode = p->sparse_mode;
-  a.max_keys = h->max_sk;
+  for (int c = 0; c <= kTopkClasses; ++c) a.row_class[c] = h->row_class[c];
   const hipError_t e = launch_topk(*p, a, (hipStream_t)stream);
   LI_CHECK(e == hipSuccess, LI_ERR_HIP, "top-k kernel launch: %s", hipGetErrorString(e));
   return LI_OK;

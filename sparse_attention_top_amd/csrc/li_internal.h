@@ -15,12 +15,28 @@ namespace li {
 //
 //   [MetaHeader][BatchRec x batch][WorkItem x num_items]
 //
+//   [MetaHeader][BatchRec x batch][WorkItem x num_items][RowRec x num_rows]
+//
 // Each BatchRec describes one sequence; each WorkItem is one workgroup of the
 // score kernel: query rows [q0, q0 + tile_q) of sequence b against keys
-// [k0, k1). Items are sorted by descending visible-pair count.
+// [k0, k1). Items are sorted by descending visible-pair count. Each RowRec is
+// one output row for the top-k kernels, grouped by size class (visible keys)
+// and, inside a class, longest row first.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMetaMagic = 0x444D494Cu;  // "LIMD"
-constexpr uint32_t kMetaVersion = 1;
+constexpr uint32_t kMetaVersion = 2;
+
+// Top-k size classes: class c holds the rows of at most kTopkClassKeys[c]
+// visible keys (the last class is unbounded) and runs with kTopkClassThreads[c]
+// threads per row.
+constexpr int kTopkClasses = 6;
+constexpr int kTopkClassKeys[kTopkClasses] = {2048, 4096, 8192, 16384, 32768, 0x7FFFFFFF};
+constexpr int kTopkClassThreads[kTopkClasses] = {256, 256, 256, 512, 1024, 1024};
+inline int topk_class(int n) {
+  int c = 0;
+  while (c + 1 < kTopkClasses && n > kTopkClassKeys[c]) ++c;
+  return c;
+}
 
 struct MetaHeader {
   uint32_t magic;
@@ -39,7 +55,8 @@ struct MetaHeader {
   uint64_t off_items;      // byte offset of the WorkItem array
   int32_t max_sk;
   int32_t max_sq;
-  int32_t reserved[10];
+  uint64_t off_rows;       // byte offset of the RowRec array
+  int32_t row_class[kTopkClasses + 2];   // first RowRec of each class; [kTopkClasses] = num_rows
 };
 static_assert(sizeof(MetaHeader) == 128, "header size");
 
@@ -58,6 +75,12 @@ struct WorkItem {
   int32_t b, q0, k0, k1;
 };
 static_assert(sizeof(WorkItem) == 16, "work item size");
+
+struct RowRec {
+  int32_t row;   // output row (B*S1 rows for BSND, T1 for TND)
+  int32_t b;     // its sequence
+};
+static_assert(sizeof(RowRec) == 8, "row record size");
 
 // Score-kernel variants: 8 waves of one query row each, arranged as WQ rows x
 // WK key slices; KT keys staged in LDS per step.
@@ -96,13 +119,12 @@ struct ScoreArgs {
 struct TopkArgs {
   const float* ws;
   const BatchRec* batches;
+  const RowRec* rows;
   int32_t* out_idx;
   float* out_val;          // may be null
-  int64_t num_rows;
-  int32_t batch;
   int32_t k;
   int32_t sparse_mode;
-  int32_t max_keys;        // longest row (visible keys), picks the register tiling
+  int32_t row_class[kTopkClasses + 1];   // class boundaries in rows (host copy)
 };
 
 // Host launchers (defined next to their kernels).

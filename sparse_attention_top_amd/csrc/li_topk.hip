@@ -9,8 +9,10 @@
 // wanted set is exactly the k largest composites and the wanted order is
 // descending composite order.
 //
-// One 256-thread workgroup per output row. Rows of up to R*256 keys stay in
-// registers for every pass ("resident"); longer rows are re-read from memory.
+// One workgroup per output row. Rows are grouped by the host into size classes
+// (visible keys); each class runs a kernel whose NT threads keep the row in
+// registers (R scores per thread, loaded as float4) or, past 32K keys, re-read
+// it from memory on every pass.
 //
 // Fast path (any row whose scores spread over a finite range):
 //   1. min / max of the row (block reduction);
@@ -22,9 +24,8 @@
 //   4. every key in a bucket >= t is written to its bucket's segment in LDS
 //      (a counting sort by bucket);
 //   5. each such key's rank inside its segment (a count of larger composites;
-//      segments are short) gives its final sorted position; keys of bucket t
-//      ranked past what is still needed are dropped; the sorted winners are
-//      permuted in LDS and written out with coalesced stores.
+//      segments are short) gives its final sorted position, where it is stored;
+//      keys of bucket t ranked past what is still needed are dropped.
 // Fallback (zero or non-finite range, or a bucket >= t holding more than
 // kSegMax keys, e.g. many equal scores): MSD radix select over the composite
 // with 11/11/10-bit digits (score first, index digits only on ties at the
@@ -35,7 +36,6 @@ namespace li {
 namespace {
 
 constexpr int kMaxK = 2048;
-constexpr int kThreads = 256;
 constexpr int kBuckets = 2048;
 constexpr int kSegMax = 64;
 constexpr int kBufCap = kMaxK + kSegMax;
@@ -58,9 +58,21 @@ __device__ inline unsigned long long composite(float s, int j) {
   return ((unsigned long long)ord_bits(s) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)j);
 }
 
+__device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFFFFFFFFu - (uint32_t)c); }
+
+template <int NT>
+struct Smem {
+  uint32_t cnt[kBuckets];                // bucket counts, then offsets
+  unsigned long long buf[kBufCap];       // composites grouped by bucket
+  uint32_t s_wave[NT / 64];
+  float s_red[2 * (NT / 64)];
+  uint32_t s_sel[4];
+};
+
 // Exclusive prefix sum over the block in thread order.
+template <int NT>
 __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave) {
-  constexpr int NW = kThreads / 64;
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -75,12 +87,12 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave) {
 #pragma unroll
   for (int w = 0; w < NW; ++w)
     if (w < wave) before += s_wave[w];
-  __syncthreads();
   return before + x - v;
 }
 
+template <int NT>
 __device__ inline void block_minmax(float& lo, float& hi, float* s_red) {
-  constexpr int NW = kThreads / 64;
+  constexpr int NW = NT / 64;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     lo = fminf(lo, __shfl_xor(lo, o));
@@ -99,71 +111,94 @@ __device__ inline void block_minmax(float& lo, float& hi, float* s_red) {
     lo = fminf(lo, s_red[w]);
     hi = fmaxf(hi, s_red[NW + w]);
   }
-  __syncthreads();
 }
 
-struct Smem {
-  uint32_t cnt[kBuckets + 64];           // bucket counts / offsets (+ one dummy per lane)
-  unsigned long long buf[kBufCap + 64];  // composites by bucket (+ one sink per lane)
-  uint32_t s_wave[kThreads / 64];
-  float s_red[2 * (kThreads / 64)];
-  uint32_t s_sel[8];
-};
-
 // Monotone map of [lo, hi] onto bucket indices 0..kBuckets-1 (one rounding, so
-// every pass computes the same bucket for the same score).
+// every pass computes the same bucket for the same score). The clamp covers
+// both ends: when |lo| is large against the range, the rounded offset can put
+// lo slightly outside [0, kBuckets).
 struct Bucketing {
   float scale, off;
   __device__ int operator()(float x) const {
-    const int b = (int)fmaf(x, scale, off);
+    const float f = fmaf(x, scale, off);
+    const int b = f > 0.f ? (int)f : 0;
     return b < kBuckets - 1 ? b : kBuckets - 1;
   }
 };
 
-// The row's scores: in registers (R per thread, element j = tid + r*kThreads)
-// when RES, else streamed from memory on every pass.
-template <int R, bool RES>
+// The row's n scores. RES: in registers, thread t holding the float4 groups
+// t + NT*v (v < R/4), i.e. key 4*(t + NT*v) + e in x[4v + e]. Otherwise they
+// are streamed from memory on every pass, with the same key-to-thread map.
+template <int NT, int R, bool RES>
 struct Row {
-  const float* src;
+  static_assert(R % 4 == 0, "whole float4 groups per thread");
+  const float* src;   // 16-byte aligned, readable up to the float4 group holding key n-1
   int n;
-  float x[RES ? R : 1];
+  float x[RES ? R : 4];
 
-  // f(x, j, slot) for every element j < n (slot is the register slot if RES).
+  __device__ inline float4 group(int v) const {   // float4 group v, clamped in range
+    const int last = (n - 1) >> 2;
+    return reinterpret_cast<const float4*>(src)[v < last ? v : last];
+  }
+
+  __device__ inline void load() {
+    if constexpr (RES) {
+#pragma unroll
+      for (int v = 0; v < R / 4; ++v) {
+        if (4 * NT * v >= n) break;   // uniform
+        const float4 g = group(threadIdx.x + NT * v);
+        x[4 * v] = canon(g.x);
+        x[4 * v + 1] = canon(g.y);
+        x[4 * v + 2] = canon(g.z);
+        x[4 * v + 3] = canon(g.w);
+      }
+    }
+  }
+
+  // f(score, key) for every key < n.
   template <typename F>
   __device__ inline void each(F&& f) const {
     if constexpr (RES) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (r * kThreads >= n) break;                 // uniform: no element left
-        const int j = threadIdx.x + r * kThreads;
-        if (j < n) f(x[r], j, r);
+      for (int v = 0; v < R / 4; ++v) {
+        if (4 * NT * v >= n) break;   // uniform
+        const int j0 = 4 * (threadIdx.x + NT * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + e < n) f(x[4 * v + e], j0 + e);
       }
     } else {
-      // Streamed: batches of kBatch independent loads keep many requests in flight.
-      constexpr int kBatch = 8;
-      for (int j0 = threadIdx.x; j0 < n; j0 += kBatch * kThreads) {
-        float v[kBatch];
+      constexpr int kBatch = 4;   // float4 groups in flight per thread
+      for (int v0 = threadIdx.x; 4 * v0 < n; v0 += kBatch * NT) {
+        float4 g[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) g[u] = group(v0 + u * NT);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          const int j = j0 + u * kThreads;
-          v[u] = j < n ? src[j] : 0.f;
-        }
+          const int j0 = 4 * (v0 + u * NT);
+          const float s[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int j = j0 + u * kThreads;
-          if (j < n) f(canon(v[u]), j, 0);
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e < n) f(canon(s[e]), j0 + e);
         }
       }
     }
   }
 };
 
+// Unused output slots [m, K): index -1, value -inf.
+__device__ inline void fill_tail(int m, int K, int32_t* oi, float* ov, int nt) {
+  for (int e = m + (int)threadIdx.x; e < K; e += nt) {
+    oi[e] = -1;
+    if (ov) ov[e] = -__builtin_huge_valf();
+  }
+}
+
 // Fast path; returns false (before writing any output) if it cannot handle the row.
-template <int R, bool RES>
-__device__ bool select_by_buckets(const Row<R, RES>& row, float lo, float hi, int K, int m,
-                                  int32_t* oi, float* ov, Smem& sm) {
+template <int NT, int R, bool RES>
+__device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi, int K, int m,
+                                  int32_t* oi, float* ov, Smem<NT>& sm) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int n = row.n;
   const float range = hi - lo;
   if (!(hi > lo) || !(range <= 3.0e38f)) return false;
@@ -171,27 +206,14 @@ __device__ bool select_by_buckets(const Row<R, RES>& row, float lo, float hi, in
   if (!(scale <= 3.0e38f)) return false;
   const Bucketing bucket{scale, -lo * scale};
 
-  for (int b = tid; b < kBuckets + 64; b += kThreads) sm.cnt[b] = 0u;
+  for (int b = tid; b < kBuckets; b += NT) sm.cnt[b] = 0u;
   if (tid == 0) sm.s_sel[2] = 0u;
   __syncthreads();
-
-  // Histogram. Resident rows keep each slot's bucket for the scatter pass.
-  int bk[RES ? R : 1];
-  if constexpr (RES) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r * kThreads >= n) break;
-      const int j = tid + r * kThreads;
-      bk[r] = j < n ? bucket(row.x[r]) : kBuckets + lane;
-      atomicAdd(&sm.cnt[bk[r]], 1u);
-    }
-  } else {
-    row.each([&](float x, int, int) { atomicAdd(&sm.cnt[bucket(x)], 1u); });
-  }
+  row.each([&](float x, int) { atomicAdd(&sm.cnt[bucket(x)], 1u); });
   __syncthreads();
 
-  // Thread t owns buckets kBuckets-1 - (t*BPT + q), i.e. a descending run.
-  constexpr int BPT = kBuckets / kThreads;
+  // Thread t owns buckets kBuckets-1 - (t*BPT + q), a descending run.
+  constexpr int BPT = kBuckets / NT;
   uint32_t c[BPT];
   uint32_t local = 0;
 #pragma unroll
@@ -199,13 +221,13 @@ __device__ bool select_by_buckets(const Row<R, RES>& row, float lo, float hi, in
     c[q] = sm.cnt[kBuckets - 1 - (tid * BPT + q)];
     local += c[q];
   }
-  const uint32_t before = block_exclusive_scan(local, sm.s_wave);
+  const uint32_t before = block_exclusive_scan<NT>(local, sm.s_wave);
   if (n <= K) {
     if (tid == 0) {
       sm.s_sel[0] = 0u;           // every bucket is taken whole
       sm.s_sel[1] = 0xFFFFFFFFu;
     }
-  } else {
+  } else if (before < (uint32_t)K && (uint32_t)K <= before + local) {
     uint32_t cum = before;
 #pragma unroll
     for (int q = 0; q < BPT; ++q) {
@@ -219,7 +241,7 @@ __device__ bool select_by_buckets(const Row<R, RES>& row, float lo, float hi, in
   __syncthreads();
   const int t = (int)sm.s_sel[0];
   const uint32_t need = sm.s_sel[1];
-  // Counts become exclusive offsets (from the top bucket); largest segment >= t.
+  // Counts become exclusive offsets from the top bucket; largest segment >= t.
   uint32_t cum = before, big = 0;
 #pragma unroll
   for (int q = 0; q < BPT; ++q) {
@@ -228,89 +250,71 @@ __device__ bool select_by_buckets(const Row<R, RES>& row, float lo, float hi, in
     cum += c[q];
     if (b >= t && c[q] > big) big = c[q];
   }
-  if (big > 0) atomicMax(&sm.s_sel[2], big);
+  if (big > (uint32_t)kSegMax) atomicMax(&sm.s_sel[2], big);
   __syncthreads();
-  if (sm.s_sel[2] > (uint32_t)kSegMax) return false;
+  if (sm.s_sel[2] != 0u) return false;
 
   // Counting sort of the keys of buckets >= t into their bucket segments.
-  // Keys that do not take part hit a per-lane dummy counter and sink slot, so
-  // the resident loop has no per-slot branch. Afterwards bucket b's segment is
-  // [cnt[b+1], cnt[b]) (cnt[kBuckets] taken as 0).
-  if constexpr (RES) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r * kThreads >= n) break;
-      const int j = tid + r * kThreads;
-      const bool take = bk[r] >= t && bk[r] < kBuckets;
-      const uint32_t pos = atomicAdd(&sm.cnt[take ? bk[r] : kBuckets + lane], 1u);
-      sm.buf[take ? pos : (uint32_t)(kBufCap + lane)] = composite(row.x[r], j);
-    }
-  } else {
-    row.each([&](float x, int j, int) {
-      const int b = bucket(x);
-      if (b >= t) sm.buf[atomicAdd(&sm.cnt[b], 1u)] = composite(x, j);
-    });
-  }
+  // Afterwards bucket b's segment is [cnt[b+1], cnt[b]) (cnt[kBuckets] = 0).
+  row.each([&](float x, int j) {
+    const int b = bucket(x);
+    if (b >= t) sm.buf[atomicAdd(&sm.cnt[b], 1u)] = composite(x, j);
+  });
   __syncthreads();
 
-  // Rank each grouped key inside its segment: its sorted position is the
-  // segment start plus the number of larger composites in the segment.
+  // Rank every grouped key inside its segment and store it at its sorted
+  // position. Four candidates per thread are ranked together so that their
+  // LDS reads overlap.
   const uint32_t ncand = sm.cnt[t];
-  constexpr int PER = (kBufCap + kThreads - 1) / kThreads;
-  unsigned long long keyv[PER];
-  int dest[PER];
+  for (uint32_t p0 = tid; p0 < ncand; p0 += 4 * NT) {
+    unsigned long long me[4];
+    uint32_t s0[4], s1[4], rank[4];
+    int bk[4];
+    uint32_t len = 0;
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const uint32_t p = tid + q * kThreads;
-    dest[q] = -1;
-    keyv[q] = 0ull;
-    if (p < ncand) {
-      const unsigned long long me = sm.buf[p];
-      const int b = bucket(from_ord((uint32_t)(me >> 32)));
-      const uint32_t s0 = b == kBuckets - 1 ? 0u : sm.cnt[b + 1];
-      const uint32_t s1 = sm.cnt[b];
-      uint32_t rank = 0;
-      for (uint32_t u = s0; u < s1; u += 4) {
-        const unsigned long long v0 = sm.buf[u];
-        const unsigned long long v1 = u + 1 < s1 ? sm.buf[u + 1] : 0ull;
-        const unsigned long long v2 = u + 2 < s1 ? sm.buf[u + 2] : 0ull;
-        const unsigned long long v3 = u + 3 < s1 ? sm.buf[u + 3] : 0ull;
-        rank += (v0 > me) + (v1 > me) + (v2 > me) + (v3 > me);
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t p = p0 + u * NT;
+      me[u] = sm.buf[p < ncand ? p : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      bk[u] = bucket(from_ord((uint32_t)(me[u] >> 32)));
+      s0[u] = bk[u] == kBuckets - 1 ? 0u : sm.cnt[bk[u] + 1];
+      s1[u] = p0 + u * NT < ncand ? sm.cnt[bk[u]] : s0[u];
+      rank[u] = 0;
+      len = max(len, s1[u] - s0[u]);
+    }
+    for (uint32_t i = 0; i < len; ++i) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t at = s0[u] + i;
+        if (at < s1[u]) rank[u] += sm.buf[at] > me[u] ? 1u : 0u;
       }
-      if (!(b == t && rank >= need)) dest[q] = (int)(s0 + rank);
-      keyv[q] = me;
     }
-  }
-  __syncthreads();
 #pragma unroll
-  for (int q = 0; q < PER; ++q)
-    if (dest[q] >= 0) sm.buf[dest[q]] = keyv[q];
-  __syncthreads();
-  for (int e = tid; e < K; e += kThreads) {
-    int32_t idx = -1;
-    float val = -__builtin_huge_valf();
-    if (e < m) {
-      const unsigned long long cv = sm.buf[e];
-      idx = (int32_t)(0xFFFFFFFFu - (uint32_t)cv);
-      val = from_ord((uint32_t)(cv >> 32));
+    for (int u = 0; u < 4; ++u) {
+      if (s0[u] < s1[u] && !(bk[u] == t && rank[u] >= need)) {
+        const uint32_t d = s0[u] + rank[u];
+        oi[d] = index_of(me[u]);
+        if (ov) ov[d] = from_ord((uint32_t)(me[u] >> 32));
+      }
     }
-    oi[e] = idx;
-    if (ov) ov[e] = val;
   }
+  fill_tail(m, K, oi, ov, NT);
   return true;
 }
 
 // Fallback: exact radix select over the composite, then bitonic sort.
-template <int R, bool RES>
-__device__ void select_by_radix(const Row<R, RES>& row, int K, int m, int32_t* oi, float* ov,
-                                Smem& sm) {
+template <int NT, int R, bool RES>
+__device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_t* oi, float* ov,
+                                Smem<NT>& sm) {
   const int tid = threadIdx.x;
   const int n = row.n;
   int P = 1;
   while (P < m) P <<= 1;
   if (n <= K) {
-    row.each([&](float x, int j, int) { sm.buf[j] = composite(x, j); });
-    for (int j = n + tid; j < P; j += kThreads) sm.buf[j] = 0ull;
+    row.each([&](float x, int j) { sm.buf[j] = composite(x, j); });
+    for (int j = n + tid; j < P; j += NT) sm.buf[j] = 0ull;
   } else {
     const int kShift[6] = {53, 42, 32, 21, 10, 0};
     const int kBits[6] = {11, 11, 10, 11, 11, 10};
@@ -321,19 +325,20 @@ __device__ void select_by_radix(const Row<R, RES>& row, int K, int m, int32_t* o
       const int shift = kShift[p];
       const int nb = 1 << kBits[p];
       const uint32_t mask = (uint32_t)nb - 1u;
-      for (int b = tid; b < nb; b += kThreads) sm.cnt[b] = 0u;
+      for (int b = tid; b < nb; b += NT) sm.cnt[b] = 0u;
       __syncthreads();
       const unsigned long long hp = fixed >= 64 ? 0ull : (prefix >> fixed);
-      row.each([&](float x, int j, int) {
+      row.each([&](float x, int j) {
         const unsigned long long cv = composite(x, j);
         if (fixed >= 64 || (cv >> fixed) == hp)
           atomicAdd(&sm.cnt[(uint32_t)(cv >> shift) & mask], 1u);
       });
       __syncthreads();
-      const int bpt = nb / kThreads;
+      // Digit buckets nb-1 .. 0 split into NT runs (nb >= NT: 1024 and 2048 buckets).
+      const int bpt = nb / NT;
       uint32_t local = 0;
       for (int q = 0; q < bpt; ++q) local += sm.cnt[nb - 1 - (tid * bpt + q)];
-      const uint32_t before = block_exclusive_scan(local, sm.s_wave);
+      const uint32_t before = block_exclusive_scan<NT>(local, sm.s_wave);
       if (before < need && need <= before + local) {
         uint32_t cum = before;
         for (int q = 0; q < bpt; ++q) {
@@ -359,19 +364,19 @@ __device__ void select_by_radix(const Row<R, RES>& row, int K, int m, int32_t* o
     }
     if (tid == 0) sm.s_sel[3] = 0u;
     __syncthreads();
-    row.each([&](float x, int j, int) {
+    row.each([&](float x, int j) {
       const unsigned long long cv = composite(x, j);
       if (cv >= prefix) {
         const uint32_t pos = atomicAdd(&sm.s_sel[3], 1u);
         if (pos < (uint32_t)K) sm.buf[pos] = cv;
       }
     });
-    for (int j = K + tid; j < P; j += kThreads) sm.buf[j] = 0ull;
+    for (int j = K + tid; j < P; j += NT) sm.buf[j] = 0ull;
   }
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int x = tid; x < (P >> 1); x += kThreads) {
+      for (int x = tid; x < (P >> 1); x += NT) {
         const int pos = 2 * x - (x & (stride - 1));
         const int oth = pos + stride;
         const bool desc = (pos & size) == 0;
@@ -384,100 +389,75 @@ __device__ void select_by_radix(const Row<R, RES>& row, int K, int m, int32_t* o
       __syncthreads();
     }
   }
-  for (int e = tid; e < K; e += kThreads) {
-    int32_t idx = -1;
-    float val = -__builtin_huge_valf();
-    if (e < m) {
-      const unsigned long long cv = sm.buf[e];
-      idx = (int32_t)(0xFFFFFFFFu - (uint32_t)cv);
-      val = from_ord((uint32_t)(cv >> 32));
-    }
-    oi[e] = idx;
-    if (ov) ov[e] = val;
+  for (int e = tid; e < m; e += NT) {
+    const unsigned long long cv = sm.buf[e];
+    oi[e] = index_of(cv);
+    if (ov) ov[e] = from_ord((uint32_t)(cv >> 32));
   }
+  fill_tail(m, K, oi, ov, NT);
 }
 
-template <int R, bool RES>
-__device__ void select_row(const float* src, int n, int K, int m, int32_t* oi, float* ov,
-                           Smem& sm) {
-  Row<R, RES> row;
-  row.src = src;
-  row.n = n;
-  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
-  if constexpr (RES) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r * kThreads >= n) break;
-      const int j = threadIdx.x + r * kThreads;
-      row.x[r] = j < n ? canon(src[j]) : 0.f;
-    }
+// One workgroup per row of one size class: row record first + blockIdx.x.
+template <int NT, int R, bool RES>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int first) {
+  __shared__ Smem<NT> sm;
+  const RowRec rr = a.rows[first + blockIdx.x];
+  const BatchRec br = a.batches[rr.b];
+  const int i = rr.row - br.row_base;
+  const int n = i < br.s_q ? visible_keys(i, br.s_q, br.s_k, a.sparse_mode) : 0;
+  const int K = a.k;
+  const int m = n < K ? n : K;
+  int32_t* oi = a.out_idx + (int64_t)rr.row * K;
+  float* ov = a.out_val ? a.out_val + (int64_t)rr.row * K : nullptr;
+  if (n == 0) {
+    fill_tail(0, K, oi, ov, NT);
+    return;
   }
-  row.each([&](float x, int, int) {
+  Row<NT, R, RES> row;
+  row.src = a.ws + br.ws_off + (int64_t)i * br.ld;
+  row.n = n;
+  row.load();
+  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+  row.each([&](float x, int) {
     lo = fminf(lo, x);
     hi = fmaxf(hi, x);
   });
-  block_minmax(lo, hi, sm.s_red);
-  if (!select_by_buckets<R, RES>(row, lo, hi, K, m, oi, ov, sm)) {
+  block_minmax<NT>(lo, hi, sm.s_red);
+  if (!select_by_buckets<NT, R, RES>(row, lo, hi, K, m, oi, ov, sm)) {
     __syncthreads();
-    select_by_radix<R, RES>(row, K, m, oi, ov, sm);
+    select_by_radix<NT, R, RES>(row, K, m, oi, ov, sm);
   }
 }
 
-// One workgroup per row. RES: this launch handles the rows of at most R*256
-// visible keys (kept in registers); otherwise it handles the longer rows
-// (streamed). Rows of the other kind return at once, so two launches cover
-// every row with each kernel compiled for its own register budget.
-template <int R, bool RES>
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
-  __shared__ Smem sm;
-  const int tid = threadIdx.x;
-  const int64_t r = blockIdx.x;
-
-  // sequence of this row: the last record with row_base <= r
-  int lo_b = 0, hi_b = a.batch - 1;
-  while (lo_b < hi_b) {
-    const int mid = (lo_b + hi_b + 1) >> 1;
-    if (a.batches[mid].row_base <= r) lo_b = mid; else hi_b = mid - 1;
-  }
-  const BatchRec br = a.batches[lo_b];
-  const int i = (int)(r - br.row_base);
-  const int n = i < br.s_q ? visible_keys(i, br.s_q, br.s_k, a.sparse_mode) : 0;
-  if ((n <= R * kThreads) != RES) return;
-  const int K = a.k;
-  const int m = n < K ? n : K;
-  int32_t* oi = a.out_idx + r * K;
-  float* ov = a.out_val ? a.out_val + r * K : nullptr;
-  if (n == 0) {
-    for (int e = tid; e < K; e += kThreads) {
-      oi[e] = -1;
-      if (ov) ov[e] = -__builtin_huge_valf();
-    }
-    return;
-  }
-  const float* src = a.ws + br.ws_off + (int64_t)i * br.ld;
-  select_row<R, RES>(src, n, K, m, oi, ov, sm);
+template <int NT, int R, bool RES>
+hipError_t launch_class(const TopkArgs& a, int c, hipStream_t s) {
+  const int first = a.row_class[c];
+  const int count = a.row_class[c + 1] - first;
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL((topk_kernel<NT, R, RES>), dim3((unsigned)count), dim3(NT), 0, s, a, first);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_topk(const li_problem& p, const TopkArgs& a, hipStream_t s) {
   (void)p;
-  if (a.num_rows <= 0) return hipSuccess;
   if (a.k < 1 || a.k > kMaxK) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)a.num_rows), block(kThreads);
-  if (a.max_keys <= 8 * kThreads) {
-    hipLaunchKernelGGL((topk_kernel<8, true>), grid, block, 0, s, a);
-  } else if (a.max_keys <= 16 * kThreads) {
-    hipLaunchKernelGGL((topk_kernel<16, true>), grid, block, 0, s, a);
-  } else {
-    hipLaunchKernelGGL((topk_kernel<32, true>), grid, block, 0, s, a);
-    if (a.max_keys > 32 * kThreads) {
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((topk_kernel<32, false>), grid, block, 0, s, a);
-    }
-  }
-  return hipGetLastError();
+  // Resident capacities NT*R must equal the class limits kTopkClassKeys.
+  static_assert(256 * 8 == kTopkClassKeys[0] && 256 * 16 == kTopkClassKeys[1] &&
+                    256 * 32 == kTopkClassKeys[2] && 512 * 32 == kTopkClassKeys[3] &&
+                    1024 * 32 == kTopkClassKeys[4],
+                "class capacities");
+  static_assert(kTopkClassThreads[0] == 256 && kTopkClassThreads[3] == 512 &&
+                    kTopkClassThreads[4] == 1024 && kTopkClassThreads[5] == 1024,
+                "class thread counts");
+  hipError_t e;
+  if ((e = launch_class<256, 8, true>(a, 0, s)) != hipSuccess) return e;
+  if ((e = launch_class<256, 16, true>(a, 1, s)) != hipSuccess) return e;
+  if ((e = launch_class<256, 32, true>(a, 2, s)) != hipSuccess) return e;
+  if ((e = launch_class<512, 32, true>(a, 3, s)) != hipSuccess) return e;
+  if ((e = launch_class<1024, 32, true>(a, 4, s)) != hipSuccess) return e;
+  return launch_class<1024, 4, false>(a, 5, s);
 }
 
 }  // namespace li

@@ -186,7 +186,38 @@ WORKLOADS = {
                                   seqlens_k=[5, 0, 70, 40], sparse_count=16, sparse_mode=3,
                                   seed=4),
     "paged": lambda: synth.paged_decode(B=6, lo=100, hi=900, block_size=64),
+    # one or two rows per sequence, key lengths spanning every top-k size class
+    "classes": lambda: synth.build("k", layout_q="TND", layout_k="TND", qk_dtype="bf16",
+                                   w_dtype="bf16", N1=8, D=64, seqlens_q=[1, 2, 1, 1, 2, 1, 0],
+                                   seqlens_k=[100, 3000, 5000, 9000, 20000, 40000, 7],
+                                   sparse_count=64, sparse_mode=0, seed=6),
 }
+
+
+def _row_table(wl, meta):
+    """Every output row appears once, with its sequence, in the size class of its
+    visible-key count, longest first inside a class."""
+    rows, bounds = B.parse_row_table(meta)
+    assert bounds[0] == 0 and bounds[-1] == wl.num_rows and (np.diff(bounds) >= 0).all()
+    assert sorted(int(r) for r in rows["row"]) == list(range(wl.num_rows))
+    where = {}
+    for b in range(wl.B):
+        nrows_b = (int(wl.cu_seqlens_q[b + 1]) - int(wl.cu_seqlens_q[b])
+                   if wl.layout_q == "TND" else wl.S1)
+        for i in range(nrows_b):
+            where[wl.row_of(b, i)] = (b, i)
+    assert len(where) == wl.num_rows
+    limits = (0,) + B.TOPK_CLASS_KEYS
+    for c in range(B.TOPK_CLASSES):
+        ns = []
+        for rec in rows[bounds[c]:bounds[c + 1]]:
+            b, row = int(rec["b"]), int(rec["row"])
+            bb, i = where[row]
+            assert bb == b
+            n = wl.n_valid(b, i) if i < int(wl.seqlens_q[b]) else 0
+            assert (n == 0 and c == 0) or limits[c] < n <= limits[c + 1]
+            ns.append(n)
+        assert ns == sorted(ns, reverse=True)
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -196,6 +227,7 @@ def test_metadata_covers_every_pair_once(lib, name):
     meta = B.li_metadata(dp, B.make_lengths(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.seqused_q,
                                             wl.seqused_k))
     h, recs, items = _coverage(wl, meta)
+    _row_table(wl, meta)
     assert int(h["num_rows"]) == wl.num_rows
     # workspace rows are 16-byte aligned and long enough
     for b in range(wl.B):

@@ -119,6 +119,11 @@ EDGE = {
     "i8_paged_bs16": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="i8", w_dtype="bf16",
                           N1=32, D=128, seqlens_q=[1, 2], seqlens_k=[500, 1700],
                           sparse_count=200, sparse_mode=3, block_size=16),
+    # rows in every top-k size class (256 / 512 / 1024 threads, resident and streamed)
+    "topk_classes": dict(layout_q="TND", layout_k="TND", qk_dtype="bf16", w_dtype="bf16", N1=8,
+                         D=64, seqlens_q=[1, 2, 1, 1, 2, 1, 0],
+                         seqlens_k=[100, 3000, 5000, 9000, 20000, 40000, 7],
+                         sparse_count=2048, sparse_mode=0),
     # block size that is not a power of two (division path of the block lookup)
     "paged_bs48": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16", w_dtype="f32",
                        N1=64, D=128, seqlens_q=[5, 7], seqlens_k=[300, 1000],
@@ -157,6 +162,23 @@ def test_integer_inputs_bit_exact(dt, mode):
     gi, gv = idx.cpu().numpy(), val.cpu().numpy()
     assert np.array_equal(gi, oi), "indices differ from the oracle on exact inputs"
     assert np.array_equal(gv, ov), "values differ from the oracle on exact inputs"
+
+
+@pytest.mark.parametrize("sk", [3000, 20000, 40000])
+def test_zero_weights_long_rows_use_exact_fallback(sk):
+    """All scores 0 in rows of every thread count (and the streamed class): the
+    bucket path cannot split the row, the radix fallback must return keys
+    0..k-1 in index order."""
+    wl = synth.build("zero_long", layout_q="TND", layout_k="TND", qk_dtype="bf16",
+                     w_dtype="f32", N1=8, D=64, seqlens_q=[2], seqlens_k=[sk], sparse_count=2048,
+                     sparse_mode=0, seed=11)
+    wl.w = np.zeros_like(wl.w)
+    idx, val, _, _ = I.run_workload(wl, DEV, return_value=True)
+    gi = idx.cpu().numpy().reshape(2, 2048)
+    gv = val.cpu().numpy().reshape(2, 2048)
+    for i in range(2):
+        assert gi[i].tolist() == list(range(2048))
+        assert (gv[i] == 0).all() and not np.signbit(gv[i]).any()
 
 
 def test_zero_weights_give_lowest_indices():
