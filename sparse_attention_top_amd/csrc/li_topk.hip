@@ -284,12 +284,23 @@ __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi
       rank[u] = 0;
       len = max(len, s1[u] - s0[u]);
     }
-    for (uint32_t i = 0; i < len; ++i) {
+    // Four segment positions of each of the four candidates per step: sixteen
+    // independent LDS reads (addresses clamped into the segment, out-of-range
+    // positions masked in the compare).
+    for (uint32_t i = 0; i < len; i += 4) {
+      unsigned long long v[4][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t at = s0[u] + i;
-        if (at < s1[u]) rank[u] += sm.buf[at] > me[u] ? 1u : 0u;
-      }
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t at = s0[u] + i + w;
+          v[u][w] = sm.buf[at < s1[u] ? at : s0[u]];
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          rank[u] += (s0[u] + i + w < s1[u] && v[u][w] > me[u]) ? 1u : 0u;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
