@@ -237,7 +237,7 @@ META_HEADER_DTYPE = np.dtype([
 BATCH_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("row_base", "<i4"), ("k_base", "<i4"),
                             ("s_q", "<i4"), ("s_k", "<i4"), ("ld", "<i4"), ("rows", "<i4")])
 WORK_ITEM_DTYPE = np.dtype([("b", "<i4"), ("q0", "<i4"), ("k0", "<i4"), ("k1", "<i4")])
-ROW_REC_DTYPE = np.dtype([("row", "<i4"), ("b", "<i4")])
+ROW_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("row", "<i4"), ("n", "<i4")])
 
 
 def parse_metadata(meta: np.ndarray):

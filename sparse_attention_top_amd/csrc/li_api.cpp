@@ -326,16 +326,13 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     // ---- top-k row table: rows grouped by size class, longest first ----
     const int64_t nrows = num_rows(*p);
     LI_CHECK(nrows < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED, "too many output rows");
-    struct RowCand {
-      RowRec r;
-      int32_t n;
-    };
-    std::vector<std::vector<RowCand>> by_class(kTopkClasses);
+    std::vector<std::vector<RowRec>> by_class(kTopkClasses);
     int64_t covered = 0;
     for (int b = 0; b < B; ++b) {
       for (int i = 0; i < rows[b]; ++i) {
         const int n = i < sq[b] ? visible_keys(i, sq[b], sk[b], p->sparse_mode) : 0;
-        by_class[topk_class(n)].push_back({{(int32_t)(row_base[b] + i), b}, n});
+        const int64_t off = n > 0 ? recs[b].ws_off + (int64_t)i * recs[b].ld : 0;
+        by_class[topk_class(n)].push_back({off, (int32_t)(row_base[b] + i), n});
       }
       covered += rows[b];
     }
@@ -380,9 +377,9 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     for (int c = 0; c < kTopkClasses; ++c) {
       auto& v = by_class[c];
       std::stable_sort(v.begin(), v.end(),
-                       [](const RowCand& x, const RowCand& y) { return x.n > y.n; });
+                       [](const RowRec& x, const RowRec& y) { return x.n > y.n; });
       h.row_class[c] = pos;
-      for (const RowCand& rc : v) rrecs[pos++] = rc.r;
+      for (const RowRec& rc : v) rrecs[pos++] = rc;
     }
     h.row_class[kTopkClasses] = pos;
     std::memcpy(dst, &h, sizeof h);
@@ -474,12 +471,10 @@ li_status li_topk(const li_problem* p, const void* meta_host, const void* meta_d
   LI_CHECK(((uintptr_t)ws % 16) == 0, LI_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   TopkArgs a;
   a.ws = static_cast<const float*>(ws);
-  a.batches = meta_ptr<BatchRec>(meta_dev, h->off_batches);
   a.rows = meta_ptr<RowRec>(meta_dev, h->off_rows);
   a.out_idx = sparse_indices;
   a.out_val = p->return_value ? sparse_values : nullptr;
   a.k = p->sparse_count;
-  a.sparse_mode = p->sparse_mode;
   for (int c = 0; c <= kTopkClasses; ++c) a.row_class[c] = h->row_class[c];
   const hipError_t e = launch_topk(*p, a, (hipStream_t)stream);
   LI_CHECK(e == hipSuccess, LI_ERR_HIP, "top-k kernel launch: %s", hipGetErrorString(e));

@@ -21,7 +21,8 @@ namespace li {
 // score kernel: query rows [q0, q0 + tile_q) of sequence b against keys
 // [k0, k1). Items are sorted by descending visible-pair count. Each RowRec is
 // one output row for the top-k kernels, grouped by size class (visible keys)
-// and, inside a class, longest row first.
+// and, inside a class, longest row first; it carries the row's visible-key
+// count and workspace offset so that a top-k workgroup needs one record.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMetaMagic = 0x444D494Cu;  // "LIMD"
 constexpr uint32_t kMetaVersion = 2;
@@ -77,10 +78,11 @@ struct WorkItem {
 static_assert(sizeof(WorkItem) == 16, "work item size");
 
 struct RowRec {
-  int32_t row;   // output row (B*S1 rows for BSND, T1 for TND)
-  int32_t b;     // its sequence
+  int64_t ws_off;  // first workspace float of the row's scores
+  int32_t row;     // output row (B*S1 rows for BSND, T1 for TND)
+  int32_t n;       // visible keys (0 for rows past a sequence's actual length)
 };
-static_assert(sizeof(RowRec) == 8, "row record size");
+static_assert(sizeof(RowRec) == 16, "row record size");
 
 // Score-kernel variants: 8 waves of one query row each, arranged as WQ rows x
 // WK key slices; KT keys staged in LDS per step.
@@ -118,12 +120,10 @@ struct ScoreArgs {
 
 struct TopkArgs {
   const float* ws;
-  const BatchRec* batches;
   const RowRec* rows;
   int32_t* out_idx;
   float* out_val;          // may be null
   int32_t k;
-  int32_t sparse_mode;
   int32_t row_class[kTopkClasses + 1];   // class boundaries in rows (host copy)
 };
 

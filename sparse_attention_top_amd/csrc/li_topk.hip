@@ -7,7 +7,7 @@
 //     c = (ord(score) << 32) | (0xFFFFFFFF - j)
 // where ord() maps float order onto unsigned order (-0 folded onto +0), so the
 // wanted set is exactly the k largest composites and the wanted order is
-// descending composite order.
+// descending composite order. Every composite is > 0.
 //
 // One workgroup per output row. Rows are grouped by the host into size classes
 // (visible keys); each class runs a kernel whose NT threads keep the row in
@@ -16,16 +16,16 @@
 //
 // Fast path (any row whose scores spread over a finite range):
 //   1. min / max of the row (block reduction);
-//   2. histogram over 2048 buckets linear in the score between min and max
-//      (monotone in the score, so bucket order is score order, and contention on
-//      the LDS counters stays low because the buckets follow the data's range);
+//   2. histogram over 4096 buckets linear in the score between min and max
+//      (monotone in the score, so bucket order is score order; the buckets follow
+//      the data's range, so they stay short);
 //   3. a block scan from the top bucket down finds the bucket t holding the k-th
 //      largest and turns the counts into each bucket's output offset;
 //   4. every key in a bucket >= t is written to its bucket's segment in LDS
 //      (a counting sort by bucket);
-//   5. each such key's rank inside its segment (a count of larger composites;
-//      segments are short) gives its final sorted position, where it is stored;
-//      keys of bucket t ranked past what is still needed are dropped.
+//   5. each such key's rank inside its segment (a count of larger composites)
+//      gives its final sorted position, where it is stored; keys of bucket t
+//      ranked past what is still needed are dropped.
 // Fallback (zero or non-finite range, or a bucket >= t holding more than
 // kSegMax keys, e.g. many equal scores): MSD radix select over the composite
 // with 11/11/10-bit digits (score first, index digits only on ties at the
@@ -36,9 +36,14 @@ namespace li {
 namespace {
 
 constexpr int kMaxK = 2048;
-constexpr int kBuckets = 2048;
-constexpr int kSegMax = 64;
+constexpr int kBuckets = 4096;        // fast-path histogram
+constexpr int kRadixBins = 2048;      // fallback digit histogram
+constexpr int kSegMax = 64;           // longest bucket segment the rank step takes
 constexpr int kBufCap = kMaxK + kSegMax;
+// Zero composites after the candidates: the rank step of a key may read up to
+// kSegMax + 1 slots past the end of its segment (they hold smaller composites
+// of later segments, or these zeros, and never count).
+constexpr int kBufPad = kSegMax + 4;
 
 // -0 -> +0 (IEEE: -0 + +0 = +0; every other value is unchanged).
 __device__ inline float canon(float x) { return x + 0.0f; }
@@ -60,13 +65,39 @@ __device__ inline unsigned long long composite(float s, int j) {
 
 __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFFFFFFFFu - (uint32_t)c); }
 
-template <int NT>
+// W16: bucket counters are 16-bit halves of 32-bit words (rows of at most 65535
+// keys), else whole 32-bit words. Counter word i lives at word i + i/8 (one pad
+// word after every eight), so that the block scan, where each thread walks a run
+// of eight consecutive counter words, reads LDS without bank conflicts.
+constexpr int padded(int i) { return i + (i >> 3); }
+template <bool W16> constexpr int kCounterWords = W16 ? kBuckets / 2 : kBuckets;
+
+template <int NT, bool W16>
 struct Smem {
-  uint32_t cnt[kBuckets];                // bucket counts, then offsets
-  unsigned long long buf[kBufCap];       // composites grouped by bucket
+  uint32_t cnt[padded(kCounterWords<W16>)];   // histogram, offsets; radix digits
+  unsigned long long buf[kBufCap + kBufPad];  // composites grouped by bucket
   uint32_t s_wave[NT / 64];
   float s_red[2 * (NT / 64)];
   uint32_t s_sel[4];
+};
+static_assert(kBuckets / 2 >= kRadixBins, "radix digits reuse the histogram words");
+
+template <bool W16>
+struct Counters {
+  uint32_t* w;
+  __device__ uint32_t& word(int i) const { return w[padded(i)]; }
+  __device__ uint32_t get(int b) const {
+    if constexpr (W16) return (word(b >> 1) >> ((b & 1) << 4)) & 0xFFFFu;
+    else return word(b);
+  }
+  __device__ void add(int b) const {
+    if constexpr (W16) atomicAdd(&word(b >> 1), 1u << ((b & 1) << 4));
+    else atomicAdd(&word(b), 1u);
+  }
+  __device__ uint32_t fetch_add(int b) const {
+    if constexpr (W16) return (atomicAdd(&word(b >> 1), 1u << ((b & 1) << 4)) >> ((b & 1) << 4)) & 0xFFFFu;
+    else return atomicAdd(&word(b), 1u);
+  }
 };
 
 // Exclusive prefix sum over the block in thread order.
@@ -120,9 +151,8 @@ __device__ inline void block_minmax(float& lo, float& hi, float* s_red) {
 struct Bucketing {
   float scale, off;
   __device__ int operator()(float x) const {
-    const float f = fmaf(x, scale, off);
-    const int b = f > 0.f ? (int)f : 0;
-    return b < kBuckets - 1 ? b : kBuckets - 1;
+    const int b = (int)fmaf(x, scale, off);
+    return min(max(b, 0), kBuckets - 1);
   }
 };
 
@@ -155,7 +185,36 @@ struct Row {
     }
   }
 
-  // f(score, key) for every key < n.
+  // f(x[4], first key, keys of the group below n) for every float4 group that
+  // holds keys < n.
+  template <typename F>
+  __device__ inline void each4(F&& f) const {
+    if constexpr (RES) {
+#pragma unroll
+      for (int v = 0; v < R / 4; ++v) {
+        if (4 * NT * v >= n) break;   // uniform
+        const int j0 = 4 * (threadIdx.x + NT * v);
+        const float g[4] = {x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+        if (j0 < n) f(g, j0, min(4, n - j0));
+      }
+    } else {
+      constexpr int kBatch = 4;   // float4 groups in flight per thread
+      for (int v0 = threadIdx.x; 4 * v0 < n; v0 += kBatch * NT) {
+        float4 q[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) q[u] = group(v0 + u * NT);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int j0 = 4 * (v0 + u * NT);
+          const float g[4] = {canon(q[u].x), canon(q[u].y), canon(q[u].z), canon(q[u].w)};
+          if (j0 < n) f(g, j0, min(4, n - j0));
+        }
+      }
+    }
+  }
+
+  // f(score, key) for every key < n. Groups that lie wholly below n (known for
+  // the whole block) skip the per-key bound test.
   template <typename F>
   __device__ inline void each(F&& f) const {
     if constexpr (RES) {
@@ -163,9 +222,14 @@ struct Row {
       for (int v = 0; v < R / 4; ++v) {
         if (4 * NT * v >= n) break;   // uniform
         const int j0 = 4 * (threadIdx.x + NT * v);
+        if (4 * NT * (v + 1) <= n) {  // uniform
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (j0 + e < n) f(x[4 * v + e], j0 + e);
+          for (int e = 0; e < 4; ++e) f(x[4 * v + e], j0 + e);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e < n) f(x[4 * v + e], j0 + e);
+        }
       }
     } else {
       constexpr int kBatch = 4;   // float4 groups in flight per thread
@@ -195,9 +259,10 @@ __device__ inline void fill_tail(int m, int K, int32_t* oi, float* ov, int nt) {
 }
 
 // Fast path; returns false (before writing any output) if it cannot handle the row.
-template <int NT, int R, bool RES>
+// The histogram words must be zero on entry.
+template <int NT, int R, bool RES, bool W16>
 __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi, int K, int m,
-                                  int32_t* oi, float* ov, Smem<NT>& sm) {
+                                  int32_t* oi, float* ov, Smem<NT, W16>& sm) {
   const int tid = threadIdx.x;
   const int n = row.n;
   const float range = hi - lo;
@@ -205,23 +270,33 @@ __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi
   const float scale = (float)kBuckets / range;
   if (!(scale <= 3.0e38f)) return false;
   const Bucketing bucket{scale, -lo * scale};
+  const Counters<W16> cnt{sm.cnt};
 
-  for (int b = tid; b < kBuckets; b += NT) sm.cnt[b] = 0u;
-  if (tid == 0) sm.s_sel[2] = 0u;
-  __syncthreads();
-  row.each([&](float x, int) { atomicAdd(&sm.cnt[bucket(x)], 1u); });
+  row.each([&](float x, int) { cnt.add(bucket(x)); });
   __syncthreads();
 
-  // Thread t owns buckets kBuckets-1 - (t*BPT + q), a descending run.
+  // Thread t owns the counter words of buckets kBuckets-1 - (t*BPT + q), a
+  // descending run of WPT words kept in registers through the scan.
   constexpr int BPT = kBuckets / NT;
-  uint32_t c[BPT];
+  constexpr int BPW = W16 ? 2 : 1;          // buckets per counter word
+  constexpr int WPT = BPT / BPW;
+  static_assert(BPT % 2 == 0, "whole 16-bit counter pairs per thread");
+  // word of the thread's q-th bucket pair (descending): covers buckets
+  // kBuckets-1 - (tid*BPT + BPW*q) and, for W16, the one below it
+  const int w_top = kCounterWords<W16> - 1 - tid * WPT;
+  uint32_t word[WPT];
   uint32_t local = 0;
 #pragma unroll
-  for (int q = 0; q < BPT; ++q) {
-    c[q] = sm.cnt[kBuckets - 1 - (tid * BPT + q)];
-    local += c[q];
+  for (int q = 0; q < WPT; ++q) {
+    word[q] = cnt.word(w_top - q);
+    local += W16 ? (word[q] >> 16) + (word[q] & 0xFFFFu) : word[q];
   }
   const uint32_t before = block_exclusive_scan<NT>(local, sm.s_wave);
+  // Counts in descending bucket order: for W16 the high half (odd bucket) first.
+  auto count_at = [&](int q, int h) -> uint32_t {   // h = 0: higher bucket of the word
+    if constexpr (W16) return h == 0 ? word[q] >> 16 : word[q] & 0xFFFFu;
+    else return word[q];
+  };
   if (n <= K) {
     if (tid == 0) {
       sm.s_sel[0] = 0u;           // every bucket is taken whole
@@ -230,42 +305,69 @@ __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi
   } else if (before < (uint32_t)K && (uint32_t)K <= before + local) {
     uint32_t cum = before;
 #pragma unroll
-    for (int q = 0; q < BPT; ++q) {
-      if (cum < (uint32_t)K && (uint32_t)K <= cum + c[q]) {
-        sm.s_sel[0] = (uint32_t)(kBuckets - 1 - (tid * BPT + q));
-        sm.s_sel[1] = (uint32_t)K - cum;
+    for (int q = 0; q < WPT; ++q)
+#pragma unroll
+      for (int h = 0; h < BPW; ++h) {
+        const uint32_t c = count_at(q, h);
+        if (cum < (uint32_t)K && (uint32_t)K <= cum + c) {
+          sm.s_sel[0] = (uint32_t)(kBuckets - 1 - (tid * BPT + BPW * q + h));
+          sm.s_sel[1] = (uint32_t)K - cum;
+        }
+        cum += c;
       }
-      cum += c[q];
-    }
   }
   __syncthreads();
   const int t = (int)sm.s_sel[0];
   const uint32_t need = sm.s_sel[1];
-  // Counts become exclusive offsets from the top bucket; largest segment >= t.
+  // Counts become exclusive offsets from the top bucket (16-bit fields are each
+  // written on their own, so a field that wraps below t cannot spill into its
+  // neighbour; only buckets >= t are used, and their offsets stay below
+  // K + kSegMax). Track the largest segment at or above t.
   uint32_t cum = before, big = 0;
 #pragma unroll
-  for (int q = 0; q < BPT; ++q) {
-    const int b = kBuckets - 1 - (tid * BPT + q);
-    sm.cnt[b] = cum;
-    cum += c[q];
-    if (b >= t && c[q] > big) big = c[q];
+  for (int q = 0; q < WPT; ++q) {
+    const int b_hi = kBuckets - 1 - (tid * BPT + BPW * q);
+    if constexpr (W16) {
+      const uint32_t c_hi = count_at(q, 0), c_lo = count_at(q, 1);
+      cnt.word(w_top - q) = ((cum & 0xFFFFu) << 16) | ((cum + c_hi) & 0xFFFFu);
+      cum += c_hi + c_lo;
+      if (b_hi >= t && c_hi > big) big = c_hi;
+      if (b_hi - 1 >= t && c_lo > big) big = c_lo;
+    } else {
+      const uint32_t c = count_at(q, 0);
+      cnt.word(w_top - q) = cum;
+      cum += c;
+      if (b_hi >= t && c > big) big = c;
+    }
   }
   if (big > (uint32_t)kSegMax) atomicMax(&sm.s_sel[2], big);
   __syncthreads();
   if (sm.s_sel[2] != 0u) return false;
 
   // Counting sort of the keys of buckets >= t into their bucket segments.
-  // Afterwards bucket b's segment is [cnt[b+1], cnt[b]) (cnt[kBuckets] = 0).
-  row.each([&](float x, int j) {
-    const int b = bucket(x);
-    if (b >= t) sm.buf[atomicAdd(&sm.cnt[b], 1u)] = composite(x, j);
+  // Afterwards bucket b's segment is [end(b+1), end(b)) (end(kBuckets) = 0).
+  row.each4([&](const float (&x)[4], int j0, int valid) {
+    int b[4];
+    uint32_t pos[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {   // all four fetch-adds in flight before any write
+      b[e] = bucket(x[e]);
+      if (e < valid && b[e] >= t) pos[e] = cnt.fetch_add(b[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < valid && b[e] >= t) sm.buf[pos[e]] = composite(x[e], j0 + e);
   });
+  __syncthreads();
+  const uint32_t ncand = cnt.get(t);
+  for (int e = tid; e < kBufPad; e += NT) sm.buf[ncand + e] = 0ull;
   __syncthreads();
 
   // Rank every grouped key inside its segment and store it at its sorted
-  // position. Four candidates per thread are ranked together so that their
-  // LDS reads overlap.
-  const uint32_t ncand = sm.cnt[t];
+  // position. Four candidates per thread are ranked together; each step reads
+  // two consecutive slots of each segment. Slots past a segment's end hold
+  // smaller composites (later segments, or the zero pad), so they never count
+  // and need no mask.
   for (uint32_t p0 = tid; p0 < ncand; p0 += 4 * NT) {
     unsigned long long me[4];
     uint32_t s0[4], s1[4], rank[4];
@@ -279,28 +381,21 @@ __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       bk[u] = bucket(from_ord((uint32_t)(me[u] >> 32)));
-      s0[u] = bk[u] == kBuckets - 1 ? 0u : sm.cnt[bk[u] + 1];
-      s1[u] = p0 + u * NT < ncand ? sm.cnt[bk[u]] : s0[u];
+      s0[u] = bk[u] == kBuckets - 1 ? 0u : cnt.get(bk[u] + 1);
+      s1[u] = p0 + u * NT < ncand ? cnt.get(bk[u]) : s0[u];
       rank[u] = 0;
       len = max(len, s1[u] - s0[u]);
     }
-    // Four segment positions of each of the four candidates per step: sixteen
-    // independent LDS reads (addresses clamped into the segment, out-of-range
-    // positions masked in the compare).
-    for (uint32_t i = 0; i < len; i += 4) {
-      unsigned long long v[4][4];
+    for (uint32_t i = 0; i < len; i += 2) {
+      unsigned long long v[4][2];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t at = s0[u] + i + w;
-          v[u][w] = sm.buf[at < s1[u] ? at : s0[u]];
-        }
+        for (int w = 0; w < 2; ++w) v[u][w] = sm.buf[s0[u] + i + w];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          rank[u] += (s0[u] + i + w < s1[u] && v[u][w] > me[u]) ? 1u : 0u;
+        for (int w = 0; w < 2; ++w) rank[u] += v[u][w] > me[u] ? 1u : 0u;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -316,11 +411,12 @@ __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi
 }
 
 // Fallback: exact radix select over the composite, then bitonic sort.
-template <int NT, int R, bool RES>
+template <int NT, int R, bool RES, bool W16>
 __device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_t* oi, float* ov,
-                                Smem<NT>& sm) {
+                                Smem<NT, W16>& sm) {
   const int tid = threadIdx.x;
   const int n = row.n;
+  uint32_t* cnt = sm.cnt;   // kRadixBins 32-bit counters
   int P = 1;
   while (P < m) P <<= 1;
   if (n <= K) {
@@ -336,25 +432,25 @@ __device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_
       const int shift = kShift[p];
       const int nb = 1 << kBits[p];
       const uint32_t mask = (uint32_t)nb - 1u;
-      for (int b = tid; b < nb; b += NT) sm.cnt[b] = 0u;
+      for (int b = tid; b < nb; b += NT) cnt[b] = 0u;
       __syncthreads();
       const unsigned long long hp = fixed >= 64 ? 0ull : (prefix >> fixed);
       row.each([&](float x, int j) {
         const unsigned long long cv = composite(x, j);
         if (fixed >= 64 || (cv >> fixed) == hp)
-          atomicAdd(&sm.cnt[(uint32_t)(cv >> shift) & mask], 1u);
+          atomicAdd(&cnt[(uint32_t)(cv >> shift) & mask], 1u);
       });
       __syncthreads();
       // Digit buckets nb-1 .. 0 split into NT runs (nb >= NT: 1024 and 2048 buckets).
       const int bpt = nb / NT;
       uint32_t local = 0;
-      for (int q = 0; q < bpt; ++q) local += sm.cnt[nb - 1 - (tid * bpt + q)];
+      for (int q = 0; q < bpt; ++q) local += cnt[nb - 1 - (tid * bpt + q)];
       const uint32_t before = block_exclusive_scan<NT>(local, sm.s_wave);
       if (before < need && need <= before + local) {
         uint32_t cum = before;
         for (int q = 0; q < bpt; ++q) {
           const int bkt = nb - 1 - (tid * bpt + q);
-          const uint32_t h = sm.cnt[bkt];
+          const uint32_t h = cnt[bkt];
           if (cum + h >= need) {
             sm.s_sel[0] = (uint32_t)bkt;
             sm.s_sel[1] = cum;
@@ -367,11 +463,11 @@ __device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_
       __syncthreads();
       const uint32_t bkt = sm.s_sel[0];
       need -= sm.s_sel[1];
-      const uint32_t cnt = sm.s_sel[2];
+      const uint32_t cnt_t = sm.s_sel[2];
       prefix |= (unsigned long long)bkt << shift;
       fixed = shift;
       __syncthreads();
-      if (cnt == need) break;
+      if (cnt_t == need) break;
     }
     if (tid == 0) sm.s_sel[3] = 0u;
     __syncthreads();
@@ -409,13 +505,12 @@ __device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_
 }
 
 // One workgroup per row of one size class: row record first + blockIdx.x.
-template <int NT, int R, bool RES>
+// W16 (16-bit bucket counters) is used only for rows of at most 65535 keys.
+template <int NT, int R, bool RES, bool W16>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int first) {
-  __shared__ Smem<NT> sm;
+  __shared__ Smem<NT, W16> sm;
   const RowRec rr = a.rows[first + blockIdx.x];
-  const BatchRec br = a.batches[rr.b];
-  const int i = rr.row - br.row_base;
-  const int n = i < br.s_q ? visible_keys(i, br.s_q, br.s_k, a.sparse_mode) : 0;
+  const int n = rr.n;
   const int K = a.k;
   const int m = n < K ? n : K;
   int32_t* oi = a.out_idx + (int64_t)rr.row * K;
@@ -425,27 +520,33 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int first) {
     return;
   }
   Row<NT, R, RES> row;
-  row.src = a.ws + br.ws_off + (int64_t)i * br.ld;
+  row.src = a.ws + rr.ws_off;
   row.n = n;
   row.load();
+  // Clear the histogram while the row loads.
+  for (int w = threadIdx.x; w < (int)(sizeof(sm.cnt) / 4); w += NT) sm.cnt[w] = 0u;
+  if (threadIdx.x == 0) sm.s_sel[2] = 0u;
   float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
   row.each([&](float x, int) {
     lo = fminf(lo, x);
     hi = fmaxf(hi, x);
   });
   block_minmax<NT>(lo, hi, sm.s_red);
-  if (!select_by_buckets<NT, R, RES>(row, lo, hi, K, m, oi, ov, sm)) {
+  const bool fast = (!W16 || n <= 65535) &&
+                    select_by_buckets<NT, R, RES, W16>(row, lo, hi, K, m, oi, ov, sm);
+  if (!fast) {
     __syncthreads();
-    select_by_radix<NT, R, RES>(row, K, m, oi, ov, sm);
+    select_by_radix<NT, R, RES, W16>(row, K, m, oi, ov, sm);
   }
 }
 
-template <int NT, int R, bool RES>
+template <int NT, int R, bool RES, bool W16>
 hipError_t launch_class(const TopkArgs& a, int c, hipStream_t s) {
   const int first = a.row_class[c];
   const int count = a.row_class[c + 1] - first;
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL((topk_kernel<NT, R, RES>), dim3((unsigned)count), dim3(NT), 0, s, a, first);
+  hipLaunchKernelGGL((topk_kernel<NT, R, RES, W16>), dim3((unsigned)count), dim3(NT), 0, s, a,
+                     first);
   return hipGetLastError();
 }
 
@@ -463,12 +564,12 @@ hipError_t launch_topk(const li_problem& p, const TopkArgs& a, hipStream_t s) {
                     kTopkClassThreads[4] == 1024 && kTopkClassThreads[5] == 1024,
                 "class thread counts");
   hipError_t e;
-  if ((e = launch_class<256, 8, true>(a, 0, s)) != hipSuccess) return e;
-  if ((e = launch_class<256, 16, true>(a, 1, s)) != hipSuccess) return e;
-  if ((e = launch_class<256, 32, true>(a, 2, s)) != hipSuccess) return e;
-  if ((e = launch_class<512, 32, true>(a, 3, s)) != hipSuccess) return e;
-  if ((e = launch_class<1024, 32, true>(a, 4, s)) != hipSuccess) return e;
-  return launch_class<1024, 4, false>(a, 5, s);
+  if ((e = launch_class<256, 8, true, true>(a, 0, s)) != hipSuccess) return e;
+  if ((e = launch_class<256, 16, true, true>(a, 1, s)) != hipSuccess) return e;
+  if ((e = launch_class<256, 32, true, true>(a, 2, s)) != hipSuccess) return e;
+  if ((e = launch_class<512, 32, true, true>(a, 3, s)) != hipSuccess) return e;
+  if ((e = launch_class<1024, 32, true, true>(a, 4, s)) != hipSuccess) return e;
+  return launch_class<1024, 4, false, false>(a, 5, s);
 }
 
 }  // namespace li

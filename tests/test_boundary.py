@@ -195,8 +195,10 @@ WORKLOADS = {
 
 
 def _row_table(wl, meta):
-    """Every output row appears once, with its sequence, in the size class of its
-    visible-key count, longest first inside a class."""
+    """Every output row appears once, with its visible-key count and the workspace
+    offset of its scores, in the size class of that count, longest first inside a
+    class."""
+    recs = B.parse_metadata(meta)[1]
     rows, bounds = B.parse_row_table(meta)
     assert bounds[0] == 0 and bounds[-1] == wl.num_rows and (np.diff(bounds) >= 0).all()
     assert sorted(int(r) for r in rows["row"]) == list(range(wl.num_rows))
@@ -211,10 +213,12 @@ def _row_table(wl, meta):
     for c in range(B.TOPK_CLASSES):
         ns = []
         for rec in rows[bounds[c]:bounds[c + 1]]:
-            b, row = int(rec["b"]), int(rec["row"])
-            bb, i = where[row]
-            assert bb == b
+            row = int(rec["row"])
+            b, i = where[row]
             n = wl.n_valid(b, i) if i < int(wl.seqlens_q[b]) else 0
+            assert int(rec["n"]) == n
+            if n > 0:
+                assert int(rec["ws_off"]) == int(recs[b]["ws_off"]) + i * int(recs[b]["ld"])
             assert (n == 0 and c == 0) or limits[c] < n <= limits[c + 1]
             ns.append(n)
         assert ns == sorted(ns, reverse=True)
