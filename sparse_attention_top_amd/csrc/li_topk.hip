@@ -506,8 +506,13 @@ __device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_
 
 // One workgroup per row of one size class: row record first + blockIdx.x.
 // W16 (16-bit bucket counters) is used only for rows of at most 65535 keys.
+// A row's latency is a chain of dependent LDS and memory steps, so throughput
+// comes from rows in flight: the 256-thread kernels are held to the register
+// budget of five (8K-key rows) or six (shorter rows) workgroups per CU, six
+// being also what the LDS allows.
 template <int NT, int R, bool RES, bool W16>
-__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a, int first) {
+__global__ __launch_bounds__(NT, NT == 256 ? (R == 32 ? 5 : 6) : 1) void topk_kernel(TopkArgs a,
+                                                                                     int first) {
   __shared__ Smem<NT, W16> sm;
   const RowRec rr = a.rows[first + blockIdx.x];
   const int n = rr.n;
