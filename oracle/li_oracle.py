@@ -29,13 +29,22 @@ with largest first and sorted output):
 3. decode the stored codes to float64 exactly (own IEEE-field decoders);
 4. s_j in float64 as above (a float64 matrix product is the dot step);
 5. order the visible keys by (s desc, j asc), keep the first m = min(k, n);
-6. sparse_indices = those j then -1; sparse_values = float32(s_j) then -inf
-   (fill values from the LightningIndexerV2 guide's constraint list).
+6. sparse_indices = those j (plus the batch's output_idx_offset, when one is
+   given) then -1; sparse_values = float32(s_j) then -inf (fill values from the
+   LightningIndexerV2 guide's constraint list).
+
+Compressed keys (the LightningIndexerV2 guide's cmp_ratio r and
+cmp_residual_k): k then holds S_k compressed keys of a sequence of
+S_k * r + residual original tokens; the scores are computed on the compressed
+keys as above, only the causal visibility changes (step 2).
 
 Readings where the pages are silent (all listed in the design notes):
 lowest index wins ties; output sorted by score; indices are 0-based positions
 within the sequence; query rows past the actual query length are all padding;
-sparse_values are float32.
+sparse_values are float32; compressed key j summarises original tokens
+[j*r, j*r + r - 1] and becomes visible under the right-down rule once its last
+token does; output_idx_offset is one non-negative value per batch, added to
+the valid indices only.
 
 Every function here is pinned by ``tests/test_oracle.py`` against closed
 forms, hand-worked examples, brute force or library routines.
@@ -140,16 +149,38 @@ def batch_lengths(wl) -> List[Tuple[int, int]]:
     return out
 
 
-def visible_count(i: int, sq: int, sk: int, mode: int) -> int:
+def visible_count(i: int, sq: int, sk: int, mode: int, cmp_ratio: int = 1,
+                  residual: int = 0) -> int:
     """Keys visible to query row i: all of them for mode 0; the right-down
-    causal rule j <= i + (S_k - S_q) for mode 3."""
+    causal rule j <= i + (S_k - S_q) for mode 3.
+
+    With compressed keys (ratio r, residual res < r) the sequence has
+    L = S_k * r + res original tokens and compressed key j covers original
+    tokens j*r .. j*r + r - 1; it is visible to row i when its last token is,
+    i.e. j*r + r - 1 <= i + L - S_q, so the first
+    clamp(floor((i + 1 + L - S_q) / r), 0, S_k) compressed keys are visible
+    (r = 1, res = 0 gives the plain rule)."""
     if i >= sq:
         return 0
     if mode == 0:
         return sk
     if mode == 3:
-        return max(0, min(sk, i + 1 + sk - sq))
+        orig = sk * cmp_ratio + residual
+        return max(0, min(sk, (i + 1 + orig - sq) // cmp_ratio))
     raise ValueError(f"sparse_mode {mode} is not defined")
+
+
+def compression(wl, b: int) -> Tuple[int, int]:
+    """(cmp_ratio, residual of batch b) of a workload; (1, 0) when uncompressed."""
+    r = int(getattr(wl, "cmp_ratio", 1) or 1)
+    res = getattr(wl, "cmp_residual_k", None)
+    return r, (int(res[b]) if res is not None else 0)
+
+
+def index_offset(wl, b: int) -> int:
+    """output_idx_offset of batch b (0 when none is given)."""
+    off = getattr(wl, "output_idx_offset", None)
+    return int(off[b]) if off is not None else 0
 
 
 # ---------------------------------------------------------------------------
@@ -264,8 +295,10 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
         by_batch.setdefault(b, []).append(r)
     for b, rlist in by_batch.items():
         sq, sk = lengths[b]
+        cr, res = compression(wl, b)
+        off = index_offset(wl, b)
         live = [r for r in rlist if rows[r][1] < sq and
-                visible_count(rows[r][1], sq, sk, wl.sparse_mode) > 0]
+                visible_count(rows[r][1], sq, sk, wl.sparse_mode, cr, res) > 0]
         if not live:
             continue
         keys, kscale = _key_block(wl, b, sk)
@@ -274,7 +307,7 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
             pos = np.array([rows[r][1] for r in chunk])
             q, w, qs = _query_block(wl, b, pos)
             for t, r in enumerate(chunk):
-                n = visible_count(int(pos[t]), sq, sk, wl.sparse_mode)
+                n = visible_count(int(pos[t]), sq, sk, wl.sparse_mode, cr, res)
                 for h in range(N2):
                     g = slice(h * G, (h + 1) * G)
                     s = row_scores(q[t, g], w[t, g], keys[:n, h],
@@ -282,7 +315,7 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
                                    None if kscale is None else kscale[:n, h])
                     order = topk_order(s, kk)
                     m = order.shape[0]
-                    idx[r, h, :m] = order
+                    idx[r, h, :m] = order + off
                     val[r, h, :m] = s[order].astype(np.float32)
                     if want_scores:
                         scores[r][h] = s

@@ -106,6 +106,50 @@ def test_visible_count_rules():
         O.visible_count(0, 1, 1, 1)
 
 
+def _visible_by_tokens(i, sq, sk, r, res):
+    """Compressed visibility counted from its definition: compressed key j
+    stands for original tokens j*r .. j*r + r - 1 of a sequence of sk*r + res
+    tokens, and is visible when every one of them is visible to row i under the
+    plain right-down rule t <= i + L - S_q."""
+    L = sk * r + res
+    return sum(all(t <= i + L - sq for t in range(j * r, j * r + r)) for j in range(sk))
+
+
+def test_visible_count_compressed_matches_token_definition():
+    for r in (1, 2, 3, 4, 8):
+        for res in range(r):
+            for sk in (0, 1, 2, 5, 9):
+                for sq in (1, 2, 4, 7, 20, 45):
+                    for i in range(sq):
+                        assert O.visible_count(i, sq, sk, 3, r, res) == \
+                            _visible_by_tokens(i, sq, sk, r, res), (i, sq, sk, r, res)
+                        assert O.visible_count(i, sq, sk, 0, r, res) == sk
+
+
+def test_visible_count_compressed_pages_example():
+    """The V2 guide's example: S2 = 130 original keys, cmp_ratio 4, so 32
+    compressed keys and residual 2, with S1 = 64 queries in mask mode 3. The
+    last query row stands at the last original token and sees every compressed
+    key; counts never decrease down the rows."""
+    counts = [O.visible_count(i, 64, 130 // 4, 3, 4, 130 % 4) for i in range(64)]
+    assert counts[-1] == 32
+    assert all(a <= b for a, b in zip(counts, counts[1:]))
+    # row 0 stands at original position 66: tokens 0..63 are complete keys 0..15
+    assert counts[0] == 16
+
+
+def test_output_offset_shifts_valid_indices_only():
+    case = dict(next(c for c in _CASES if c["name"] == "C_causal"))
+    base = O.run(_hand_workload(case))
+    wl = _hand_workload(case)
+    wl.output_idx_offset = np.array([7], np.int32)
+    shifted = O.run(wl)
+    bi, si = base["indices"], shifted["indices"]
+    assert (si[bi < 0] == -1).all() and (bi < 0).any()
+    assert np.array_equal(si[bi >= 0], bi[bi >= 0] + 7)
+    assert np.array_equal(base["values"], shifted["values"])
+
+
 # ---------------------------------------------------------------------------
 # hand-worked examples
 # ---------------------------------------------------------------------------
@@ -141,6 +185,11 @@ def _hand_workload(case):
         ns.w = wv
         ns.k = _enc(np.array(case["keys"])[:, None, :], dt)
         return ns
+    ns.cmp_ratio = case.get("cmp_ratio", 1)
+    ns.cmp_residual_k = (np.array(case["cmp_residual_k"], np.int32)
+                         if "cmp_residual_k" in case else None)
+    ns.output_idx_offset = (np.array(case["output_idx_offset"], np.int32)
+                            if "output_idx_offset" in case else None)
     ns.B = 1
     ns.layout_q = "BSND"
     ns.q = _enc(qv[None], dt)
