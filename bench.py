@@ -42,9 +42,10 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-def algorithmic_score_bytes(wl):
+def algorithmic_score_bytes(wl, pairs):
     """Bytes the score kernel must move at least once: Q, W, scales, each key of
-    each sequence once, and one float32 per visible pair written."""
+    each sequence once, and one float32 per visible pair written (pairs = the
+    visible (query row, key) count of the library's task table)."""
     es = 1 if wl.qk_dtype in ("e4m3fn", "i8") else 2
     ws = 4 if wl.w_dtype == "f32" else 2
     rows = int(sum(int(x) for x in wl.seqlens_q))
@@ -52,7 +53,7 @@ def algorithmic_score_bytes(wl):
     b = rows * wl.N1 * (wl.D * es + ws) + keys * wl.N2 * wl.D * es
     if wl.quant:
         b += rows * wl.N1 * 4 + keys * wl.N2 * 4
-    return b + 4 * wl.visible_pairs()
+    return b + 4 * int(pairs)
 
 
 def cpu_baseline(wl, seconds, seed=1234):
@@ -163,10 +164,10 @@ def main():
               file=sys.stderr)
 
     rows = wl.num_rows
-    pairs = wl.visible_pairs()
+    pairs = int(plan.header["visible_pairs"])
     flops = 2.0 * wl.N1 * wl.D * pairs
     score_tflops = flops / (score_ms * 1e-3) / 1e12
-    sbytes = algorithmic_score_bytes(wl)
+    sbytes = algorithmic_score_bytes(wl, pairs)
     score_gbs = sbytes / (score_ms * 1e-3) / 1e9
     kk = wl.sparse_count
     tbytes = 4 * pairs + rows * wl.N2 * kk * (8 if p.return_value else 4)

@@ -30,10 +30,14 @@
  * Readings of points the pages leave open (also listed in the design notes):
  * keys are ranked by score, ties going to the lower key index; each output row
  * is sorted by descending score; indices are 0-based key positions within the
- * sequence (logical position for the paged layout); unused slots hold -1 in
- * sparse_indices and -inf in sparse_values; query rows past a sequence's actual
- * length are all unused slots; dequant scales must be >= 0 (they are absmax /
- * qmax by construction); NaN inputs give undefined rankings.
+ * sequence (logical position for the paged layout), plus the batch's
+ * output_idx_offset when one is given; unused slots hold -1 in sparse_indices
+ * and -inf in sparse_values; query rows past a sequence's actual length are all
+ * unused slots; dequant scales must be >= 0 (they are absmax / qmax by
+ * construction); NaN inputs give undefined rankings; with compressed keys
+ * (cmp_ratio r > 1), compressed key j stands for original tokens
+ * j*r .. j*r + r - 1 of a sequence of S_k*r + cmp_residual_k original tokens
+ * and is visible under the right-down rule once its last token is.
  */
 #ifndef LI_H_
 #define LI_H_
@@ -45,7 +49,7 @@
 extern "C" {
 #endif
 
-#define LI_API_VERSION 1
+#define LI_API_VERSION 2
 
 typedef enum li_status {
   LI_OK = 0,
@@ -97,13 +101,20 @@ typedef enum li_dtype {
  *                longest sequence (quant README constraint list).
  *  k_block_stride PA only: elements between consecutive blocks of k (0 means
  *                block_size*n2*d); models the quant README's "stride" attribute.
- *  sparse_count  k, 1..2048 (MindSpore page).
+ *  sparse_count  k, 1..8192 (MindSpore page: up to 2048; the V2 guide's
+ *                constraint list: up to 8192).
  *  sparse_mode   0 (every key of the sequence) or 3 (right-down causal: key j is
  *                visible to query row i iff j <= i + S_k - S_q, with the actual
  *                per-sequence lengths).
  *  pre_tokens, next_tokens  reserved by the pages; only INT64_MAX is accepted.
  *  return_value  0: sparse_values may be NULL; 1: sparse_values (float32, same
  *                shape as sparse_indices) is written.
+ *  cmp_ratio     key compression ratio r of the V2 guide (cmp_ratio attribute):
+ *                0 or 1 = keys are not compressed; 2..128 = k holds compressed
+ *                keys (S_k of them per sequence, lengths given in compressed
+ *                keys) and, in sparse_mode 3, cmp_residual_k gives each
+ *                sequence's leftover original tokens (row i then sees the first
+ *                clamp(floor((i + 1 + S_k*r + res - S_q) / r), 0, S_k) keys).
  */
 typedef struct li_problem {
   uint32_t api_version;   /* LI_API_VERSION */
@@ -129,7 +140,8 @@ typedef struct li_problem {
   int64_t pre_tokens;
   int64_t next_tokens;
   int32_t return_value;
-  int32_t reserved[7];    /* must be zero */
+  int32_t cmp_ratio;
+  int32_t reserved[6];    /* must be zero */
 } li_problem;
 
 /*
@@ -146,12 +158,20 @@ typedef struct li_problem {
  *  seqused_k     (B) int32: actual key lengths. Optional for BSND (<= s2) and
  *                TND (<= the cu_seqlens_k length), NULL meaning the full length;
  *                required for PA_BSND (covered by max_blocks_per_seq blocks).
+ *  cmp_residual_k (B) int32: original tokens past the last whole compressed key
+ *                of each sequence, 0 <= res < cmp_ratio (V2 guide, cmp_residual_k).
+ *                Required when cmp_ratio > 1 and sparse_mode == 3, else NULL.
+ *  output_idx_offset (B) int32, optional: a value >= 0 added to every returned
+ *                index of the sequence's rows (-1 slots unchanged); every
+ *                key index + offset must fit in int32 (V2 guide, output_idx_offset).
  */
 typedef struct li_lengths {
   const int32_t* cu_seqlens_q;
   const int32_t* cu_seqlens_k;
   const int32_t* seqused_q;
   const int32_t* seqused_k;
+  const int32_t* cmp_residual_k;
+  const int32_t* output_idx_offset;
 } li_lengths;
 
 /*

@@ -16,7 +16,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libli_mi355x.so")
 
-API_VERSION = 1
+API_VERSION = 2
 INT64_MAX = (1 << 63) - 1
 
 # li_status
@@ -72,7 +72,8 @@ class li_problem(ctypes.Structure):
         ("pre_tokens", ctypes.c_int64),
         ("next_tokens", ctypes.c_int64),
         ("return_value", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 7),
+        ("cmp_ratio", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 6),
     ]
 
 
@@ -82,6 +83,8 @@ class li_lengths(ctypes.Structure):
         ("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32)),
         ("seqused_q", ctypes.POINTER(ctypes.c_int32)),
         ("seqused_k", ctypes.POINTER(ctypes.c_int32)),
+        ("cmp_residual_k", ctypes.POINTER(ctypes.c_int32)),
+        ("output_idx_offset", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -100,7 +103,7 @@ def make_problem(*, layout_q="BSND", layout_k="BSND", dtype_qk="bf16", dtype_w="
                  dtype_scale="f32", batch=1, s1=0, s2=0, n1=64, n2=1, d=128, t1=0, t2=0,
                  block_size=0, max_blocks_per_seq=0, num_blocks=0, k_block_stride=0,
                  sparse_count=2048, sparse_mode=3, pre_tokens=INT64_MAX,
-                 next_tokens=INT64_MAX, return_value=False) -> li_problem:
+                 next_tokens=INT64_MAX, return_value=False, cmp_ratio=1) -> li_problem:
     p = li_problem()
     p.api_version = API_VERSION
     p.layout_q = LAYOUTS[layout_q] if isinstance(layout_q, str) else int(layout_q)
@@ -116,6 +119,7 @@ def make_problem(*, layout_q="BSND", layout_k="BSND", dtype_qk="bf16", dtype_w="
     p.sparse_count, p.sparse_mode = int(sparse_count), int(sparse_mode)
     p.pre_tokens, p.next_tokens = int(pre_tokens), int(next_tokens)
     p.return_value = int(bool(return_value))
+    p.cmp_ratio = int(cmp_ratio)
     return p
 
 
@@ -169,10 +173,12 @@ def _i32p(a: Optional[np.ndarray]):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def make_lengths(cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None):
+def make_lengths(cu_seqlens_q=None, cu_seqlens_k=None, seqused_q=None, seqused_k=None,
+                 cmp_residual_k=None, output_idx_offset=None):
     """Host lengths: arrays are converted to contiguous int32 and kept alive on the result."""
     keep = [None if a is None else np.ascontiguousarray(np.asarray(a), dtype=np.int32)
-            for a in (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k)]
+            for a in (cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k, cmp_residual_k,
+                      output_idx_offset)]
     L = li_lengths(*[_i32p(a) for a in keep])
     L._keep = keep  # type: ignore[attr-defined]
     return L
@@ -235,9 +241,11 @@ META_HEADER_DTYPE = np.dtype([
     ("off_rows", "<u8"), ("row_class", "<i4", (TOPK_CLASSES + 2,)),
 ])
 BATCH_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("row_base", "<i4"), ("k_base", "<i4"),
-                            ("s_q", "<i4"), ("s_k", "<i4"), ("ld", "<i4"), ("rows", "<i4")])
+                            ("s_q", "<i4"), ("s_k", "<i4"), ("ld", "<i4"), ("rows", "<i4"),
+                            ("cmp_res", "<i4"), ("reserved", "<i4")])
 WORK_ITEM_DTYPE = np.dtype([("b", "<i4"), ("q0", "<i4"), ("k0", "<i4"), ("k1", "<i4")])
-ROW_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("row", "<i4"), ("n", "<i4")])
+ROW_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("row", "<i4"), ("n", "<i4"),
+                          ("idx_offset", "<i4"), ("reserved", "<i4")])
 
 
 def parse_metadata(meta: np.ndarray):

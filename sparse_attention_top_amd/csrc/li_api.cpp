@@ -109,8 +109,10 @@ li_status check_problem(const li_problem* p) {
   LI_CHECK(p->n2 == 1, LI_ERR_UNSUPPORTED, "only n2 == 1 is supported (got %d)", p->n2);
   LI_CHECK(p->n1 <= 64, LI_ERR_UNSUPPORTED, "n1 must be at most 64 (got %d)", p->n1);
   LI_CHECK(p->d == 64 || p->d == 128, LI_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", p->d);
-  LI_CHECK(p->sparse_count >= 1 && p->sparse_count <= 2048, LI_ERR_INVALID_ARGUMENT,
-           "sparse_count must be in [1, 2048] (got %d)", p->sparse_count);
+  LI_CHECK(p->sparse_count >= 1 && p->sparse_count <= 8192, LI_ERR_INVALID_ARGUMENT,
+           "sparse_count must be in [1, 8192] (got %d)", p->sparse_count);
+  LI_CHECK(p->cmp_ratio >= 0 && p->cmp_ratio <= 128, LI_ERR_INVALID_ARGUMENT,
+           "cmp_ratio must be in [0, 128] (0 and 1 mean uncompressed keys), got %d", p->cmp_ratio);
   LI_CHECK(p->sparse_mode == 0 || p->sparse_mode == 3, LI_ERR_INVALID_ARGUMENT,
            "sparse_mode must be 0 or 3 (got %d)", p->sparse_mode);
   LI_CHECK(p->pre_tokens == kInt64Max && p->next_tokens == kInt64Max, LI_ERR_UNSUPPORTED,
@@ -120,11 +122,13 @@ li_status check_problem(const li_problem* p) {
   return LI_OK;
 }
 
+int32_t cmp_ratio_of(const li_problem& p) { return p.cmp_ratio > 1 ? p.cmp_ratio : 1; }
+
 uint64_t problem_hash(const li_problem& p) {
   // FNV-1a over the fields that shape the work decomposition.
   const int64_t f[] = {p.layout_q, p.layout_k, p.dtype_qk, p.batch, p.s1, p.s2, p.n1, p.n2, p.d,
                        p.t1, p.t2, p.block_size, p.max_blocks_per_seq, p.num_blocks,
-                       p.sparse_mode};
+                       p.sparse_mode, cmp_ratio_of(p)};
   uint64_t h = 1469598103934665603ull;
   const unsigned char* b = reinterpret_cast<const unsigned char*>(f);
   for (size_t i = 0; i < sizeof f; ++i) {
@@ -257,6 +261,38 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
       }
     }
 
+    // ---- compressed keys and index offsets (V2 guide, constraint list) ----
+    const int32_t cr = cmp_ratio_of(*p);
+    std::vector<int32_t> cres(B, 0), ioff(B, 0);
+    if (cr > 1 && p->sparse_mode == 3) {
+      LI_CHECK(L->cmp_residual_k != nullptr, LI_ERR_INVALID_ARGUMENT,
+               "cmp_ratio > 1 with sparse_mode 3 needs cmp_residual_k");
+      for (int b = 0; b < B; ++b) {
+        cres[b] = L->cmp_residual_k[b];
+        LI_CHECK(cres[b] >= 0 && cres[b] < cr, LI_ERR_INVALID_ARGUMENT,
+                 "cmp_residual_k[%d]=%d outside [0, cmp_ratio=%d)", b, cres[b], cr);
+        LI_CHECK((int64_t)sk[b] * cr + cres[b] < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED,
+                 "sequence %d is longer than 2^31 original tokens", b);
+      }
+    } else {
+      LI_CHECK(L->cmp_residual_k == nullptr, LI_ERR_INVALID_ARGUMENT,
+               "cmp_residual_k is taken only with cmp_ratio > 1 and sparse_mode 3");
+    }
+    if (L->output_idx_offset) {
+      for (int b = 0; b < B; ++b) {
+        ioff[b] = L->output_idx_offset[b];
+        LI_CHECK(ioff[b] >= 0, LI_ERR_INVALID_ARGUMENT, "output_idx_offset[%d]=%d is negative", b,
+                 ioff[b]);
+        LI_CHECK((int64_t)ioff[b] + (sk[b] > 0 ? sk[b] - 1 : 0) <= 0x7FFFFFFFll,
+                 LI_ERR_INVALID_ARGUMENT,
+                 "output_idx_offset[%d]=%d pushes key index %d past INT32_MAX", b, ioff[b],
+                 sk[b] - 1);
+      }
+    }
+    auto visible = [&](int b, int i) {
+      return visible_keys(i, sq[b], sk[b], p->sparse_mode, cr, cres[b]);
+    };
+
     // ---- variant and tiling ----
     int max_sq = 0, max_sk = 0;
     for (int b = 0; b < B; ++b) {
@@ -269,7 +305,7 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
 
     int64_t pairs = 0;
     for (int b = 0; b < B; ++b)
-      for (int i = 0; i < sq[b]; ++i) pairs += visible_keys(i, sq[b], sk[b], p->sparse_mode);
+      for (int i = 0; i < sq[b]; ++i) pairs += visible(b, i);
     // Each key chunk of a row tile re-reads the tile's query heads, so rows are
     // split along keys only when there are too few row tiles to fill the CUs.
     int64_t tiles = 0;
@@ -295,6 +331,8 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
       r.s_k = sk[b];
       r.ld = std::max(4, (sk[b] + 3) / 4 * 4);
       r.rows = rows[b];
+      r.cmp_res = cres[b];
+      r.reserved = 0;
       ws += (int64_t)sq[b] * r.ld;
     }
 
@@ -307,12 +345,12 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     for (int b = 0; b < B; ++b) {
       for (int q0 = 0; q0 < sq[b]; q0 += TQ) {
         const int qe = std::min(q0 + TQ, sq[b]);
-        const int nvmax = visible_keys(qe - 1, sq[b], sk[b], p->sparse_mode);
+        const int nvmax = visible(b, qe - 1);
         for (int64_t k0 = 0; k0 < nvmax; k0 += chunk) {
           const int k1 = (int)std::min<int64_t>(k0 + chunk, nvmax);
           int64_t cost = 0;
           for (int i = q0; i < qe; ++i) {
-            const int nv = visible_keys(i, sq[b], sk[b], p->sparse_mode);
+            const int nv = visible(b, i);
             cost += std::max<int64_t>(0, std::min<int64_t>(nv, k1) - k0);
           }
           cands.push_back({{b, q0, (int)k0, k1}, cost});
@@ -330,9 +368,9 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     int64_t covered = 0;
     for (int b = 0; b < B; ++b) {
       for (int i = 0; i < rows[b]; ++i) {
-        const int n = i < sq[b] ? visible_keys(i, sq[b], sk[b], p->sparse_mode) : 0;
+        const int n = i < sq[b] ? visible(b, i) : 0;
         const int64_t off = n > 0 ? recs[b].ws_off + (int64_t)i * recs[b].ld : 0;
-        by_class[topk_class(n)].push_back({off, (int32_t)(row_base[b] + i), n});
+        by_class[topk_class(n)].push_back({off, (int32_t)(row_base[b] + i), n, ioff[b], 0});
       }
       covered += rows[b];
     }
@@ -447,6 +485,7 @@ li_status li_score(const li_problem* p, const li_inputs* in, const void* meta_ho
     if (p->block_size == (1 << sh)) a.block_shift = sh;
   a.max_blocks = p->max_blocks_per_seq;
   a.sparse_mode = p->sparse_mode;
+  a.cmp_ratio = cmp_ratio_of(*p);
   const hipError_t e = launch_score(*p, h->variant, h->num_items, a, (hipStream_t)stream);
   LI_CHECK(e == hipSuccess, LI_ERR_HIP, "score kernel launch: %s", hipGetErrorString(e));
   return LI_OK;

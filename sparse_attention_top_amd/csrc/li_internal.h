@@ -25,7 +25,7 @@ namespace li {
 // count and workspace offset so that a top-k workgroup needs one record.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMetaMagic = 0x444D494Cu;  // "LIMD"
-constexpr uint32_t kMetaVersion = 2;
+constexpr uint32_t kMetaVersion = 3;
 
 // Top-k size classes: class c holds the rows of at most kTopkClassKeys[c]
 // visible keys (the last class is unbounded) and runs with kTopkClassThreads[c]
@@ -66,11 +66,13 @@ struct BatchRec {
   int32_t row_base; // first output row == first q / w row of the sequence
   int32_t k_base;   // first key row (TND: cu_seqlens_k[b]; BSND: b*S2; PA: 0)
   int32_t s_q;      // actual query length
-  int32_t s_k;      // actual key length
+  int32_t s_k;      // actual key length (compressed keys when cmp_ratio > 1)
   int32_t ld;       // workspace row stride in floats (multiple of 4)
   int32_t rows;     // output rows allotted to the sequence (S1 for BSND, s_q for TND)
+  int32_t cmp_res;  // original tokens past the last whole compressed key (0 if none)
+  int32_t reserved;
 };
-static_assert(sizeof(BatchRec) == 32, "batch record size");
+static_assert(sizeof(BatchRec) == 40, "batch record size");
 
 struct WorkItem {
   int32_t b, q0, k0, k1;
@@ -78,11 +80,13 @@ struct WorkItem {
 static_assert(sizeof(WorkItem) == 16, "work item size");
 
 struct RowRec {
-  int64_t ws_off;  // first workspace float of the row's scores
-  int32_t row;     // output row (B*S1 rows for BSND, T1 for TND)
-  int32_t n;       // visible keys (0 for rows past a sequence's actual length)
+  int64_t ws_off;      // first workspace float of the row's scores
+  int32_t row;         // output row (B*S1 rows for BSND, T1 for TND)
+  int32_t n;           // visible keys (0 for rows past a sequence's actual length)
+  int32_t idx_offset;  // added to every returned index (output_idx_offset)
+  int32_t reserved;
 };
-static_assert(sizeof(RowRec) == 16, "row record size");
+static_assert(sizeof(RowRec) == 24, "row record size");
 
 // Score-kernel variants: 8 waves of one query row each, arranged as WQ rows x
 // WK key slices; KT keys staged in LDS per step.
@@ -116,6 +120,7 @@ struct ScoreArgs {
   int32_t block_shift;     // log2(block_size) when it is a power of two, else -1
   int32_t max_blocks;
   int32_t sparse_mode;
+  int32_t cmp_ratio;       // 1 for uncompressed keys
 };
 
 struct TopkArgs {
@@ -132,11 +137,18 @@ hipError_t launch_score(const li_problem& p, int variant, int num_items, const S
                         hipStream_t s);
 hipError_t launch_topk(const li_problem& p, const TopkArgs& a, hipStream_t s);
 
-// Visible keys of query row i (i < s_q) of a sequence with lengths (s_q, s_k).
-__host__ __device__ inline int32_t visible_keys(int32_t i, int32_t s_q, int32_t s_k, int32_t mode) {
+// Visible keys of query row i (i < s_q) of a sequence with lengths (s_q, s_k):
+// mode 0 every key; mode 3 the right-down causal rule j <= i + S_k - S_q. With
+// compressed keys (ratio r, residual res) the sequence has L = s_k*r + res
+// original tokens and compressed key j (tokens j*r .. j*r + r - 1) is visible
+// once its last token is: the first floor((i + 1 + L - s_q) / r) keys.
+__host__ __device__ inline int32_t visible_keys(int32_t i, int32_t s_q, int32_t s_k, int32_t mode,
+                                                int32_t cmp_ratio = 1, int32_t cmp_res = 0) {
   if (mode == 0) return s_k;
-  int64_t v = (int64_t)i + 1 + (int64_t)s_k - (int64_t)s_q;
-  return v < 0 ? 0 : (v > s_k ? s_k : (int32_t)v);
+  const int64_t num = (int64_t)i + 1 + (int64_t)s_k * cmp_ratio + cmp_res - (int64_t)s_q;
+  if (num < cmp_ratio) return 0;
+  const int64_t v = num / cmp_ratio;
+  return v > s_k ? s_k : (int32_t)v;
 }
 
 }  // namespace li

@@ -192,7 +192,8 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
 
   const int row = it.q0 + wq;
   const bool row_ok = row < br.s_q;
-  const int nv = row_ok ? visible_keys(row, br.s_q, br.s_k, a.sparse_mode) : 0;
+  const int nv = row_ok ? visible_keys(row, br.s_q, br.s_k, a.sparse_mode, a.cmp_ratio, br.cmp_res)
+                        : 0;
   const int lim = nv < it.k1 ? nv : it.k1;   // this row stores keys [k0, lim)
   const int64_t qrow = (int64_t)br.row_base + (row_ok ? row : 0);
   float* out_row = a.ws + br.ws_off + (int64_t)(row_ok ? row : 0) * br.ld;

@@ -1,4 +1,4 @@
-// Per-row top-k over the head-reduced scores (k <= 2048).
+// Per-row top-k over the head-reduced scores (k <= 8192).
 //
 // The selection order is (score descending, key index ascending): the pages ask
 // for a deterministic top-k (CANN LightningIndexerV2 guide, "确定性计算") and the
@@ -35,12 +35,13 @@
 namespace li {
 namespace {
 
-constexpr int kMaxK = 2048;
+constexpr int kMaxKSmall = 2048;      // k of the default kernels (LDS sized for it)
+constexpr int kMaxKLarge = 8192;      // k of the large-k kernels
 constexpr int kBuckets = 4096;        // fast-path histogram
 constexpr int kRadixBins = 2048;      // fallback digit histogram
 constexpr int kSegMax = 64;           // longest bucket segment the rank step takes
-constexpr int kBufCap = kMaxK + kSegMax;
-// Zero composites after the candidates: the rank step of a key may read up to
+// Zero composites after the candidates (at most k + kSegMax of them): the rank
+// step of a key may read up to
 // kSegMax + 1 slots past the end of its segment (they hold smaller composites
 // of later segments, or these zeros, and never count).
 constexpr int kBufPad = kSegMax + 4;
@@ -72,10 +73,10 @@ __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFF
 constexpr int padded(int i) { return i + (i >> 3); }
 template <bool W16> constexpr int kCounterWords = W16 ? kBuckets / 2 : kBuckets;
 
-template <int NT, bool W16>
+template <int NT, bool W16, int KMAX>
 struct Smem {
-  uint32_t cnt[padded(kCounterWords<W16>)];   // histogram, offsets; radix digits
-  unsigned long long buf[kBufCap + kBufPad];  // composites grouped by bucket
+  uint32_t cnt[padded(kCounterWords<W16>)];          // histogram, offsets; radix digits
+  unsigned long long buf[KMAX + kSegMax + kBufPad];  // composites grouped by bucket
   uint32_t s_wave[NT / 64];
   float s_red[2 * (NT / 64)];
   uint32_t s_sel[4];
@@ -260,9 +261,9 @@ __device__ inline void fill_tail(int m, int K, int32_t* oi, float* ov, int nt) {
 
 // Fast path; returns false (before writing any output) if it cannot handle the row.
 // The histogram words must be zero on entry.
-template <int NT, int R, bool RES, bool W16>
+template <int NT, int R, bool RES, bool W16, int KMAX>
 __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi, int K, int m,
-                                  int32_t* oi, float* ov, Smem<NT, W16>& sm) {
+                                  int32_t* oi, float* ov, int32_t ioff, Smem<NT, W16, KMAX>& sm) {
   const int tid = threadIdx.x;
   const int n = row.n;
   const float range = hi - lo;
@@ -401,7 +402,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi
     for (int u = 0; u < 4; ++u) {
       if (s0[u] < s1[u] && !(bk[u] == t && rank[u] >= need)) {
         const uint32_t d = s0[u] + rank[u];
-        oi[d] = index_of(me[u]);
+        oi[d] = index_of(me[u]) + ioff;
         if (ov) ov[d] = from_ord((uint32_t)(me[u] >> 32));
       }
     }
@@ -411,9 +412,9 @@ __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi
 }
 
 // Fallback: exact radix select over the composite, then bitonic sort.
-template <int NT, int R, bool RES, bool W16>
+template <int NT, int R, bool RES, bool W16, int KMAX>
 __device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_t* oi, float* ov,
-                                Smem<NT, W16>& sm) {
+                                int32_t ioff, Smem<NT, W16, KMAX>& sm) {
   const int tid = threadIdx.x;
   const int n = row.n;
   uint32_t* cnt = sm.cnt;   // kRadixBins 32-bit counters
@@ -498,7 +499,7 @@ __device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_
   }
   for (int e = tid; e < m; e += NT) {
     const unsigned long long cv = sm.buf[e];
-    oi[e] = index_of(cv);
+    oi[e] = index_of(cv) + ioff;
     if (ov) ov[e] = from_ord((uint32_t)(cv >> 32));
   }
   fill_tail(m, K, oi, ov, NT);
@@ -510,10 +511,10 @@ __device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_
 // comes from rows in flight: the 256-thread kernels are held to the register
 // budget of five (8K-key rows) or six (shorter rows) workgroups per CU, six
 // being also what the LDS allows.
-template <int NT, int R, bool RES, bool W16>
-__global__ __launch_bounds__(NT, NT == 256 ? (R == 32 ? 5 : 6) : 1) void topk_kernel(TopkArgs a,
-                                                                                     int first) {
-  __shared__ Smem<NT, W16> sm;
+template <int NT, int R, bool RES, bool W16, int KMAX>
+__global__ __launch_bounds__(NT, (NT == 256 && KMAX == kMaxKSmall) ? (R == 32 ? 5 : 6) : 1)
+void topk_kernel(TopkArgs a, int first) {
+  __shared__ Smem<NT, W16, KMAX> sm;
   const RowRec rr = a.rows[first + blockIdx.x];
   const int n = rr.n;
   const int K = a.k;
@@ -538,28 +539,40 @@ __global__ __launch_bounds__(NT, NT == 256 ? (R == 32 ? 5 : 6) : 1) void topk_ke
   });
   block_minmax<NT>(lo, hi, sm.s_red);
   const bool fast = (!W16 || n <= 65535) &&
-                    select_by_buckets<NT, R, RES, W16>(row, lo, hi, K, m, oi, ov, sm);
+                    select_by_buckets<NT, R, RES, W16, KMAX>(row, lo, hi, K, m, oi, ov,
+                                                             rr.idx_offset, sm);
   if (!fast) {
     __syncthreads();
-    select_by_radix<NT, R, RES, W16>(row, K, m, oi, ov, sm);
+    select_by_radix<NT, R, RES, W16, KMAX>(row, K, m, oi, ov, rr.idx_offset, sm);
   }
 }
 
-template <int NT, int R, bool RES, bool W16>
+template <int NT, int R, bool RES, bool W16, int KMAX>
 hipError_t launch_class(const TopkArgs& a, int c, hipStream_t s) {
   const int first = a.row_class[c];
   const int count = a.row_class[c + 1] - first;
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL((topk_kernel<NT, R, RES, W16>), dim3((unsigned)count), dim3(NT), 0, s, a,
-                     first);
+  hipLaunchKernelGGL((topk_kernel<NT, R, RES, W16, KMAX>), dim3((unsigned)count), dim3(NT), 0, s,
+                     a, first);
   return hipGetLastError();
+}
+
+template <int KMAX>
+hipError_t launch_all(const TopkArgs& a, hipStream_t s) {
+  hipError_t e;
+  if ((e = launch_class<256, 8, true, true, KMAX>(a, 0, s)) != hipSuccess) return e;
+  if ((e = launch_class<256, 16, true, true, KMAX>(a, 1, s)) != hipSuccess) return e;
+  if ((e = launch_class<256, 32, true, true, KMAX>(a, 2, s)) != hipSuccess) return e;
+  if ((e = launch_class<512, 32, true, true, KMAX>(a, 3, s)) != hipSuccess) return e;
+  if ((e = launch_class<1024, 32, true, true, KMAX>(a, 4, s)) != hipSuccess) return e;
+  return launch_class<1024, 4, false, false, KMAX>(a, 5, s);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const li_problem& p, const TopkArgs& a, hipStream_t s) {
   (void)p;
-  if (a.k < 1 || a.k > kMaxK) return hipErrorInvalidValue;
+  if (a.k < 1 || a.k > kMaxKLarge) return hipErrorInvalidValue;
   // Resident capacities NT*R must equal the class limits kTopkClassKeys.
   static_assert(256 * 8 == kTopkClassKeys[0] && 256 * 16 == kTopkClassKeys[1] &&
                     256 * 32 == kTopkClassKeys[2] && 512 * 32 == kTopkClassKeys[3] &&
@@ -568,13 +581,7 @@ hipError_t launch_topk(const li_problem& p, const TopkArgs& a, hipStream_t s) {
   static_assert(kTopkClassThreads[0] == 256 && kTopkClassThreads[3] == 512 &&
                     kTopkClassThreads[4] == 1024 && kTopkClassThreads[5] == 1024,
                 "class thread counts");
-  hipError_t e;
-  if ((e = launch_class<256, 8, true, true>(a, 0, s)) != hipSuccess) return e;
-  if ((e = launch_class<256, 16, true, true>(a, 1, s)) != hipSuccess) return e;
-  if ((e = launch_class<256, 32, true, true>(a, 2, s)) != hipSuccess) return e;
-  if ((e = launch_class<512, 32, true, true>(a, 3, s)) != hipSuccess) return e;
-  if ((e = launch_class<1024, 32, true, true>(a, 4, s)) != hipSuccess) return e;
-  return launch_class<1024, 4, false, false>(a, 5, s);
+  return a.k <= kMaxKSmall ? launch_all<kMaxKSmall>(a, s) : launch_all<kMaxKLarge>(a, s);
 }
 
 }  // namespace li

@@ -6,7 +6,9 @@ MindSpore ``lightning_indexer`` page (its signature and parameter list):
 ``actual_seq_lengths_query`` / ``actual_seq_lengths_key`` are per-batch
 lengths for BSND and PA_BSND, and prefix sums without the leading zero for
 TND; ``sparse_values`` comes back with shape (0,) when ``return_value`` is
-False (CANN V2 guide, return value section).
+False (CANN V2 guide, return value section). The V2 guide's compressed keys
+(``cmp_ratio``, ``cmp_residual_k``) and per-batch ``output_idx_offset`` are
+accepted as keywords too.
 """
 from __future__ import annotations
 
@@ -73,6 +75,7 @@ def lightning_indexer(query: torch.Tensor, key: torch.Tensor, weights: torch.Ten
                       next_tokens: int = B.INT64_MAX, return_value: bool = False,
                       query_dequant_scale: Optional[torch.Tensor] = None,
                       key_dequant_scale: Optional[torch.Tensor] = None,
+                      cmp_ratio: int = 1, cmp_residual_k=None, output_idx_offset=None,
                       plan: Optional[Plan] = None, num_cus: int = 256):
     """Top-k key indices (int32) and optionally values (float32) per query token."""
     dev = query.device
@@ -100,7 +103,7 @@ def lightning_indexer(query: torch.Tensor, key: torch.Tensor, weights: torch.Ten
     kw = dict(layout_q=layout_query, layout_k=layout_key, dtype_qk=dt,
               dtype_w=_W_DTYPES[weights.dtype], n1=n1, d=d, sparse_count=sparse_count,
               sparse_mode=sparse_mode, pre_tokens=pre_tokens, next_tokens=next_tokens,
-              return_value=return_value)
+              return_value=return_value, cmp_ratio=cmp_ratio)
     aq = _host_i32(actual_seq_lengths_query)
     ak = _host_i32(actual_seq_lengths_key)
     cu_q = cu_k = used_q = used_k = None
@@ -128,7 +131,8 @@ def lightning_indexer(query: torch.Tensor, key: torch.Tensor, weights: torch.Ten
     kw.update(batch=b_sz, s1=s1, t1=t1)
     p = B.make_problem(**kw)
     if plan is None:
-        plan = make_plan(p, B.make_lengths(cu_q, cu_k, used_q, used_k), dev, num_cus)
+        plan = make_plan(p, B.make_lengths(cu_q, cu_k, used_q, used_k, _host_i32(cmp_residual_k),
+                                           _host_i32(output_idx_offset)), dev, num_cus)
     n2 = p.n2
     rows = (b_sz, s1, n2, sparse_count) if layout_query == "BSND" else (t1, n2, sparse_count)
     idx = torch.empty(rows, dtype=torch.int32, device=dev)
@@ -179,7 +183,8 @@ def problem_of(wl, return_value: Optional[bool] = None) -> B.li_problem:
     rv = wl.return_value if return_value is None else return_value
     kw = dict(layout_q=wl.layout_q, layout_k=wl.layout_k, dtype_qk=wl.qk_dtype,
               dtype_w=wl.w_dtype, batch=wl.B, n1=wl.N1, n2=wl.N2, d=wl.D,
-              sparse_count=wl.sparse_count, sparse_mode=wl.sparse_mode, return_value=rv)
+              sparse_count=wl.sparse_count, sparse_mode=wl.sparse_mode, return_value=rv,
+              cmp_ratio=getattr(wl, "cmp_ratio", 1))
     if wl.layout_q == "TND":
         kw["t1"] = int(wl.q.shape[0])
     else:
@@ -196,7 +201,8 @@ def problem_of(wl, return_value: Optional[bool] = None) -> B.li_problem:
 
 def upload(wl, device="cuda", return_value: Optional[bool] = None) -> DeviceWorkload:
     p = problem_of(wl, return_value)
-    L = B.make_lengths(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.seqused_q, wl.seqused_k)
+    L = B.make_lengths(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.seqused_q, wl.seqused_k,
+                       getattr(wl, "cmp_residual_k", None), getattr(wl, "output_idx_offset", None))
     bt = None if wl.block_table is None else torch.from_numpy(wl.block_table).to(device)
     return DeviceWorkload(p, L, to_device(wl.q, wl.qk_dtype, device),
                           to_device(wl.k, wl.qk_dtype, device),

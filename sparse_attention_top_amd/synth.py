@@ -137,6 +137,9 @@ class Workload:
     seqused_k: Optional[np.ndarray] = None
     block_table: Optional[np.ndarray] = None
     block_size: int = 0
+    cmp_ratio: int = 1                          # key compression ratio (1: none)
+    cmp_residual_k: Optional[np.ndarray] = None  # (B,) leftover original tokens
+    output_idx_offset: Optional[np.ndarray] = None  # (B,) added to returned indices
     seed: int = 0
     notes: Dict[str, object] = field(default_factory=dict)
 
@@ -153,29 +156,10 @@ class Workload:
         """Output rows: B*S1 for BSND queries, T1 for TND."""
         return self.T1
 
-    def n_valid(self, b: int, i: int) -> int:
-        """Visible keys of query row i of batch b (i < actual S_q)."""
-        sq, sk = int(self.seqlens_q[b]), int(self.seqlens_k[b])
-        if self.sparse_mode == 0:
-            return sk
-        return max(0, min(sk, i + 1 + sk - sq))
-
     def row_of(self, b: int, i: int) -> int:
         if self.layout_q == "TND":
             return int(self.cu_seqlens_q[b]) + i
         return b * self.S1 + i
-
-    def visible_pairs(self) -> int:
-        tot = 0
-        for b in range(self.B):
-            sq, sk = int(self.seqlens_q[b]), int(self.seqlens_k[b])
-            if self.sparse_mode == 0:
-                tot += sq * sk
-            else:
-                off = sk - sq
-                i = np.arange(sq, dtype=np.int64)
-                tot += int(np.clip(i + 1 + off, 0, sk).sum())
-        return tot
 
 
 # --------------------------------------------------------------------------
@@ -221,7 +205,9 @@ def build(name: str, *, layout_q: str, layout_k: str, qk_dtype: str, w_dtype: st
           block_size: int = 128, max_blocks: Optional[int] = None,
           w_std: float = 1.0, seed: int = 0,
           pass_seqused_q: Optional[bool] = None,
-          pass_seqused_k: Optional[bool] = None) -> Workload:
+          pass_seqused_k: Optional[bool] = None,
+          cmp_ratio: int = 1, cmp_residual_k: Optional[Sequence[int]] = None,
+          output_idx_offset: Optional[Sequence[int]] = None) -> Workload:
     """Draw one problem. Draw order: q, k, w, then the paged block permutation."""
     if layout_k != "PA_BSND" and layout_k != layout_q:
         raise ValueError("non-paged key layout must equal the query layout")
@@ -311,6 +297,11 @@ def build(name: str, *, layout_q: str, layout_k: str, qk_dtype: str, w_dtype: st
                     return_value=bool(return_value), seqlens_q=sl_q, seqlens_k=sl_k,
                     q=q, k=k, w=w, q_scale=q_scale, k_scale=k_scale,
                     block_size=block_size if layout_k == "PA_BSND" else 0,
+                    cmp_ratio=int(cmp_ratio),
+                    cmp_residual_k=(None if cmp_residual_k is None
+                                    else np.asarray(cmp_residual_k, np.int32)),
+                    output_idx_offset=(None if output_idx_offset is None
+                                       else np.asarray(output_idx_offset, np.int32)),
                     seed=seed, **wl_kw)
 
 

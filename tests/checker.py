@@ -23,6 +23,23 @@ import numpy as np
 TOL = {"f16": 1e-3, "bf16": 1e-3, "e4m3fn": 2e-2, "i8": 2e-2}
 
 
+def visible(wl, b: int, i: int) -> int:
+    """Visible keys of row i of batch b, by the oracle's rule (0 past S_q)."""
+    from oracle import li_oracle as O
+    sq, sk = O.batch_lengths(wl)[b]
+    return O.visible_count(i, sq, sk, wl.sparse_mode, *O.compression(wl, b))
+
+
+def visible_pairs(wl) -> int:
+    """Sum of the visible keys over all rows, by the oracle's rule."""
+    from oracle import li_oracle as O
+    tot = 0
+    for b, (sq, sk) in enumerate(O.batch_lengths(wl)):
+        cr, res = O.compression(wl, b)
+        tot += sum(O.visible_count(i, sq, sk, wl.sparse_mode, cr, res) for i in range(sq))
+    return tot
+
+
 class RowStats:
     def __init__(self):
         self.rows = 0
@@ -92,13 +109,25 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
 
 
 def check_rows(gidx_rows: np.ndarray, gval_rows: Optional[np.ndarray], oracle_out: dict,
-               k: int, tol: float, label: str = "") -> RowStats:
-    """gidx_rows / gval_rows: (R, N2, k) arrays aligned with oracle_out['rows']."""
+               k: int, tol: float, label: str = "", offsets=None) -> RowStats:
+    """gidx_rows / gval_rows: (R, N2, k) arrays aligned with oracle_out['rows'].
+
+    offsets: per-batch output_idx_offset (or None); returned indices must be the
+    key index plus the offset, -1 slots stay -1, and the rule is then applied to
+    the key indices."""
     st = RowStats()
     for r, (b, i) in enumerate(oracle_out["rows"]):
         for h in range(gidx_rows.shape[1]):
-            check_row(gidx_rows[r, h], None if gval_rows is None else gval_rows[r, h],
-                      oracle_out["scores"][r][h], k, tol,
-                      oidx=oracle_out["indices"][r, h], stats=st,
+            g = np.asarray(gidx_rows[r, h]).astype(np.int64)
+            o = np.asarray(oracle_out["indices"][r, h]).astype(np.int64)
+            if offsets is not None:
+                off = int(offsets[b])
+                valid = g >= 0
+                assert (g[valid] >= off).all(), f"{label} row (b={b}, i={i}): offset not applied"
+                assert (g[~valid] == -1).all()
+                g = np.where(valid, g - off, g)
+                o = np.where(o >= 0, o - off, o)
+            check_row(g, None if gval_rows is None else gval_rows[r, h],
+                      oracle_out["scores"][r][h], k, tol, oidx=o, stats=st,
                       where=f"{label} row (b={b}, i={i})")
     return st

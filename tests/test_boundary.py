@@ -10,6 +10,7 @@ import pytest
 from sparse_attention_top_amd import binding as B
 from sparse_attention_top_amd import indexer as I
 from sparse_attention_top_amd import synth
+from tests.checker import visible, visible_pairs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -61,7 +62,9 @@ BAD = [
     ("w dtype", dict(dtype_w="e4m3fn"), B.ERR_INVALID_ARGUMENT),
     ("qk dtype", dict(dtype_qk="f32"), B.ERR_INVALID_ARGUMENT),
     ("k zero", dict(sparse_count=0), B.ERR_INVALID_ARGUMENT),
-    ("k too big", dict(sparse_count=2049), B.ERR_INVALID_ARGUMENT),
+    ("k too big", dict(sparse_count=8193), B.ERR_INVALID_ARGUMENT),
+    ("cmp ratio negative", dict(cmp_ratio=-1), B.ERR_INVALID_ARGUMENT),
+    ("cmp ratio too big", dict(cmp_ratio=129), B.ERR_INVALID_ARGUMENT),
     ("mode 1", dict(sparse_mode=1), B.ERR_INVALID_ARGUMENT),
     ("mode 2", dict(sparse_mode=2), B.ERR_INVALID_ARGUMENT),
     ("pre_tokens", dict(pre_tokens=100), B.ERR_UNSUPPORTED),
@@ -121,12 +124,28 @@ LEN_BAD = [
                                       max_blocks_per_seq=4), dict(seqused_k=[65, 3])),
     ("tnd seqused_k beyond cu", dict(layout_q="TND", layout_k="TND", t1=8, t2=8, batch=1),
      dict(cu_seqlens_q=[0, 8], cu_seqlens_k=[0, 8], seqused_k=[9])),
+    ("cmp without residual", dict(cmp_ratio=4), dict()),
+    ("cmp residual >= ratio", dict(cmp_ratio=4), dict(cmp_residual_k=[0, 4])),
+    ("cmp residual negative", dict(cmp_ratio=4), dict(cmp_residual_k=[-1, 0])),
+    ("residual without cmp", dict(), dict(cmp_residual_k=[0, 0])),
+    ("residual with ratio 1", dict(cmp_ratio=1), dict(cmp_residual_k=[0, 0])),
+    ("residual in mode 0", dict(cmp_ratio=4, sparse_mode=0), dict(cmp_residual_k=[1, 1])),
+    ("negative index offset", dict(), dict(output_idx_offset=[0, -1])),
+    ("index offset overflows", dict(), dict(output_idx_offset=[0, 2**31 - 63])),
 ]
 
 
 @pytest.mark.parametrize("name,pk,lk", LEN_BAD, ids=[b[0] for b in LEN_BAD])
 def test_length_checks(lib, name, pk, lk):
     assert _status(_prob(**pk), B.make_lengths(**lk)) == B.ERR_INVALID_ARGUMENT
+
+
+def test_compressed_original_length_limit(lib):
+    # the visibility rule works on original token positions, which must fit int32
+    p = _prob(cmp_ratio=128, s2=(1 << 24) - 1)
+    assert _status(p, B.make_lengths(cmp_residual_k=[127, 127])) == B.OK
+    p = _prob(cmp_ratio=128, s2=1 << 24)
+    assert _status(p, B.make_lengths(cmp_residual_k=[0, 0])) == B.ERR_UNSUPPORTED
 
 
 def test_buffer_too_small_reports_size(lib):
@@ -155,18 +174,18 @@ def _coverage(wl, meta):
         r = recs[b]
         assert k0 < k1
         for i in range(q0, min(q0 + tq, int(r["s_q"]))):
-            nv = wl.n_valid(b, i)
+            nv = visible(wl, b, i)
             hi = min(nv, k1)
             if hi > k0:
                 cover[b][i, k0:hi] += 1
     pairs = 0
     for b in range(wl.B):
         for i in range(int(recs[b]["s_q"])):
-            nv = wl.n_valid(b, i)
+            nv = visible(wl, b, i)
             assert (cover[b][i, :nv] == 1).all(), f"row ({b},{i}) not covered exactly once"
             assert (cover[b][i, nv:] == 0).all()
             pairs += nv
-    assert pairs == int(h["visible_pairs"]) == wl.visible_pairs()
+    assert pairs == int(h["visible_pairs"]) == visible_pairs(wl)
     return h, recs, items
 
 
@@ -191,7 +210,28 @@ WORKLOADS = {
                                    w_dtype="bf16", N1=8, D=64, seqlens_q=[1, 2, 1, 1, 2, 1, 0],
                                    seqlens_k=[100, 3000, 5000, 9000, 20000, 40000, 7],
                                    sparse_count=64, sparse_mode=0, seed=6),
+    # compressed keys: ratio 4 with per-batch residuals, and per-batch index offsets
+    "compressed": lambda: synth.build("z", layout_q="BSND", layout_k="BSND", qk_dtype="bf16",
+                                      w_dtype="bf16", N1=16, D=128, seqlens_q=[300, 7, 64],
+                                      seqlens_k=[80, 3, 20], S1=300, S2=80, sparse_count=32,
+                                      sparse_mode=3, cmp_ratio=4, cmp_residual_k=[3, 0, 1],
+                                      output_idx_offset=[0, 1000, 77], seed=7),
+    "compressed_tnd": lambda: synth.build("zt", layout_q="TND", layout_k="TND",
+                                          qk_dtype="e4m3fn", w_dtype="f32", N1=32, D=128,
+                                          seqlens_q=[128, 1, 50], seqlens_k=[1000, 9, 13],
+                                          sparse_count=16, sparse_mode=3, cmp_ratio=128,
+                                          cmp_residual_k=[127, 5, 0], seed=8),
+    "compressed_nomask": lambda: synth.build("zn", layout_q="BSND", layout_k="BSND",
+                                             qk_dtype="bf16", w_dtype="bf16", N1=8, D=64,
+                                             seqlens_q=[9, 9], seqlens_k=[40, 40],
+                                             sparse_count=8, sparse_mode=0, cmp_ratio=2,
+                                             output_idx_offset=[5, 6], seed=9),
 }
+
+
+def _lengths(wl):
+    return B.make_lengths(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.seqused_q, wl.seqused_k,
+                          wl.cmp_residual_k, wl.output_idx_offset)
 
 
 def _row_table(wl, meta):
@@ -215,8 +255,10 @@ def _row_table(wl, meta):
         for rec in rows[bounds[c]:bounds[c + 1]]:
             row = int(rec["row"])
             b, i = where[row]
-            n = wl.n_valid(b, i) if i < int(wl.seqlens_q[b]) else 0
+            n = visible(wl, b, i) if i < int(wl.seqlens_q[b]) else 0
             assert int(rec["n"]) == n
+            off = 0 if wl.output_idx_offset is None else int(wl.output_idx_offset[b])
+            assert int(rec["idx_offset"]) == off
             if n > 0:
                 assert int(rec["ws_off"]) == int(recs[b]["ws_off"]) + i * int(recs[b]["ld"])
             assert (n == 0 and c == 0) or limits[c] < n <= limits[c + 1]
@@ -228,8 +270,7 @@ def _row_table(wl, meta):
 def test_metadata_covers_every_pair_once(lib, name):
     wl = WORKLOADS[name]()
     dp = I.problem_of(wl)
-    meta = B.li_metadata(dp, B.make_lengths(wl.cu_seqlens_q, wl.cu_seqlens_k, wl.seqused_q,
-                                            wl.seqused_k))
+    meta = B.li_metadata(dp, _lengths(wl))
     h, recs, items = _coverage(wl, meta)
     _row_table(wl, meta)
     assert int(h["num_rows"]) == wl.num_rows

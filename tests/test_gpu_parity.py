@@ -15,7 +15,7 @@ from oracle import li_oracle as O
 from sparse_attention_top_amd import binding as B
 from sparse_attention_top_amd import indexer as I
 from sparse_attention_top_amd import synth
-from tests.checker import TOL, check_rows
+from tests.checker import TOL, check_rows, visible, visible_pairs
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def _row_index(wl, rows):
 
 
 def run_and_check(wl, rows=None, return_value=True, label=""):
-    _say(f"[gpu] {label or wl.name}: rows={wl.num_rows} pairs={wl.visible_pairs()}")
+    _say(f"[gpu] {label or wl.name}: rows={wl.num_rows} pairs={visible_pairs(wl)}")
     idx, val, plan, _ = I.run_workload(wl, DEV, return_value=return_value)
     torch.cuda.synchronize()
     gi = _flat_rows(wl, idx.cpu().numpy())
@@ -44,7 +44,7 @@ def run_and_check(wl, rows=None, return_value=True, label=""):
     o = O.run(wl, rows=rows, want_scores=True)
     sel = _row_index(wl, o["rows"])
     st = check_rows(gi[sel], None if gv is None else gv[sel], o, wl.sparse_count,
-                    TOL[wl.qk_dtype], label=label or wl.name)
+                    TOL[wl.qk_dtype], label=label or wl.name, offsets=wl.output_idx_offset)
     if rows is None:   # rows the oracle did not visit must not exist
         assert sel.shape[0] == gi.shape[0]
     _say(f"[gpu] {label or wl.name}: {st}")
@@ -128,6 +128,39 @@ EDGE = {
     "paged_bs48": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16", w_dtype="f32",
                        N1=64, D=128, seqlens_q=[5, 7], seqlens_k=[300, 1000],
                        sparse_count=128, sparse_mode=3, block_size=48),
+    # compressed keys (ratio 4, per-batch residuals) with per-batch index offsets
+    "cmp_bsnd_offsets": dict(layout_q="BSND", layout_k="BSND", qk_dtype="bf16", w_dtype="bf16",
+                             N1=64, D=128, seqlens_q=[300, 7, 64], seqlens_k=[80, 3, 20],
+                             S1=300, S2=80, sparse_count=32, sparse_mode=3, cmp_ratio=4,
+                             cmp_residual_k=[3, 0, 1], output_idx_offset=[0, 1000, 77]),
+    # ratio 128: many query rows share one visible count, short rows see nothing
+    "cmp_tnd_fp8": dict(layout_q="TND", layout_k="TND", qk_dtype="e4m3fn", w_dtype="f32",
+                        N1=64, D=128, seqlens_q=[128, 1, 50], seqlens_k=[1000, 9, 13],
+                        sparse_count=16, sparse_mode=3, cmp_ratio=128,
+                        cmp_residual_k=[127, 5, 0]),
+    "cmp_paged_decode": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16",
+                             w_dtype="bf16", N1=64, D=128, seqlens_q=[2, 2, 1],
+                             seqlens_k=[700, 50, 1500], sparse_count=256, sparse_mode=3,
+                             block_size=64, cmp_ratio=4, cmp_residual_k=[1, 2, 3],
+                             output_idx_offset=[0, 4096, 123]),
+    "cmp_nomask_offsets": dict(layout_q="BSND", layout_k="BSND", qk_dtype="f16", w_dtype="f32",
+                               N1=16, D=64, seqlens_q=[9, 9], seqlens_k=[40, 40],
+                               sparse_count=8, sparse_mode=0, cmp_ratio=2,
+                               output_idx_offset=[5, 6]),
+    "i8_offsets": dict(layout_q="TND", layout_k="TND", qk_dtype="i8", w_dtype="f16", N1=32,
+                       D=128, seqlens_q=[30, 0, 70], seqlens_k=[30, 0, 300], sparse_count=64,
+                       sparse_mode=3, output_idx_offset=[0, 7, 100000]),
+    # k above 2048: the large-k top-k kernels
+    "k4096_causal": dict(layout_q="BSND", layout_k="BSND", qk_dtype="bf16", w_dtype="bf16",
+                         N1=16, D=64, seqlens_q=[600], seqlens_k=[4400], sparse_count=4096,
+                         sparse_mode=3),
+    "k3072_paged": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16", w_dtype="f32",
+                        N1=64, D=128, seqlens_q=[1, 1, 1], seqlens_k=[5000, 2000, 3073],
+                        sparse_count=3072, sparse_mode=3, block_size=64),
+    "k8192_classes": dict(layout_q="TND", layout_k="TND", qk_dtype="bf16", w_dtype="bf16",
+                          N1=8, D=64, seqlens_q=[1, 2, 1, 1, 2, 1],
+                          seqlens_k=[100, 3000, 8192, 9000, 20000, 40000], sparse_count=8192,
+                          sparse_mode=0),
 }
 
 
@@ -137,13 +170,14 @@ def test_edge_cases_all_rows(name):
     run_and_check(wl, label=name)
 
 
-def _integer_workload(qk_dtype="bf16", mode=3, seed=5):
+def _integer_workload(qk_dtype="bf16", mode=3, seed=5, **extra):
     """Small-integer q/k and power-of-two weights: every score is exact in fp32,
     so GPU and oracle must agree bit for bit, ties (lowest index first) included."""
     rng = np.random.default_rng(seed)
-    wl = synth.build("int", layout_q="BSND", layout_k="BSND", qk_dtype=qk_dtype, w_dtype="f32",
-                     N1=64, D=128, seqlens_q=[150], seqlens_k=[400], sparse_count=96,
-                     sparse_mode=mode, seed=seed)
+    kw = dict(layout_q="BSND", layout_k="BSND", qk_dtype=qk_dtype, w_dtype="f32", N1=64, D=128,
+              seqlens_q=[150], seqlens_k=[400], sparse_count=96, sparse_mode=mode, seed=seed)
+    kw.update(extra)
+    wl = synth.build("int", **kw)
     q = rng.integers(-2, 3, wl.q.shape).astype(np.float32)
     k = rng.integers(-2, 3, wl.k.shape).astype(np.float32)
     if qk_dtype == "bf16":
@@ -154,9 +188,18 @@ def _integer_workload(qk_dtype="bf16", mode=3, seed=5):
     return wl
 
 
-@pytest.mark.parametrize("dt,mode", [("bf16", 3), ("f16", 0)])
-def test_integer_inputs_bit_exact(dt, mode):
-    wl = _integer_workload(dt, mode)
+INT_CASES = [
+    ("bf16", 3, {}),
+    ("f16", 0, {}),
+    ("bf16", 3, dict(cmp_ratio=4, cmp_residual_k=[2], output_idx_offset=[50])),
+    ("f16", 0, dict(sparse_count=2500, seqlens_k=[3000])),
+]
+
+
+@pytest.mark.parametrize("dt,mode,extra", INT_CASES,
+                         ids=["bf16_causal", "f16_nomask", "bf16_compressed_offset", "f16_k2500"])
+def test_integer_inputs_bit_exact(dt, mode, extra):
+    wl = _integer_workload(dt, mode, **extra)
     idx, val, _, _ = I.run_workload(wl, DEV, return_value=True)
     oi, ov = O.run_full(wl)
     gi, gv = idx.cpu().numpy(), val.cpu().numpy()
@@ -164,20 +207,22 @@ def test_integer_inputs_bit_exact(dt, mode):
     assert np.array_equal(gv, ov), "values differ from the oracle on exact inputs"
 
 
-@pytest.mark.parametrize("sk", [3000, 20000, 40000])
-def test_zero_weights_long_rows_use_exact_fallback(sk):
+@pytest.mark.parametrize("sk,k", [(3000, 2048), (20000, 2048), (40000, 2048), (5000, 4096),
+                                  (9000, 8192), (40000, 8192)])
+def test_zero_weights_long_rows_use_exact_fallback(sk, k):
     """All scores 0 in rows of every thread count (and the streamed class): the
     bucket path cannot split the row, the radix fallback must return keys
     0..k-1 in index order."""
     wl = synth.build("zero_long", layout_q="TND", layout_k="TND", qk_dtype="bf16",
-                     w_dtype="f32", N1=8, D=64, seqlens_q=[2], seqlens_k=[sk], sparse_count=2048,
+                     w_dtype="f32", N1=8, D=64, seqlens_q=[2], seqlens_k=[sk], sparse_count=k,
                      sparse_mode=0, seed=11)
     wl.w = np.zeros_like(wl.w)
+    _say(f"[gpu] zero weights sk={sk} k={k}")
     idx, val, _, _ = I.run_workload(wl, DEV, return_value=True)
-    gi = idx.cpu().numpy().reshape(2, 2048)
-    gv = val.cpu().numpy().reshape(2, 2048)
+    gi = idx.cpu().numpy().reshape(2, k)
+    gv = val.cpu().numpy().reshape(2, k)
     for i in range(2):
-        assert gi[i].tolist() == list(range(2048))
+        assert gi[i].tolist() == list(range(k))
         assert (gv[i] == 0).all() and not np.signbit(gv[i]).any()
 
 
@@ -257,7 +302,7 @@ def _sample_rows(wl, n_random=24, seed=0):
             continue
         cand = {0, sq - 1, sq // 2}
         for i in range(sq):                       # where n_valid crosses k
-            if wl.n_valid(b, i) in (wl.sparse_count, wl.sparse_count + 1):
+            if visible(wl, b, i) in (wl.sparse_count, wl.sparse_count + 1):
                 cand.add(i)
         rows.update((b, i) for i in cand if 0 <= i < sq)
     all_b = [b for b in range(wl.B) if wl.seqlens_q[b] > 0]
