@@ -38,6 +38,22 @@ cmp_residual_k): k then holds S_k compressed keys of a sequence of
 S_k * r + residual original tokens; the scores are computed on the compressed
 keys as above, only the causal visibility changes (step 2).
 
+Routing options of the forward operator the ops-transformer open-sourcing
+issue lists (part 2, "LightningIndexer 族": block_len for key-block
+granularity 1/2/4/8/16, init_num for sink tokens that are always kept,
+local_num for the diagonal local window), which the issue names but does not
+define; the oracle takes these readings:
+
+7. with block_len L > 1 the selection runs over key blocks: block c holds
+   keys [c*L, (c+1)*L) of the sequence, its score is the largest score of its
+   visible keys, and a row has ceil(n / L) visible blocks; the output indices
+   are block indices;
+8. the first init_num visible blocks and the last local_num visible blocks
+   (the latter end at the row's diagonal under the causal rule) are always
+   kept: they fill the first output slots in ascending block order, and the
+   remaining k - (number kept) slots take the other blocks ordered as in
+   step 5.
+
 Readings where the pages are silent (all listed in the design notes):
 lowest index wins ties; output sorted by score; indices are 0-based positions
 within the sequence; query rows past the actual query length are all padding;
@@ -183,6 +199,12 @@ def index_offset(wl, b: int) -> int:
     return int(off[b]) if off is not None else 0
 
 
+def routing(wl) -> Tuple[int, int, int]:
+    """(block_len, init_num, local_num) of a workload; (1, 0, 0) when not given."""
+    L = int(getattr(wl, "block_len", 1) or 1)
+    return L, int(getattr(wl, "init_num", 0) or 0), int(getattr(wl, "local_num", 0) or 0)
+
+
 # ---------------------------------------------------------------------------
 # Step 3: per-batch operand gathering
 # ---------------------------------------------------------------------------
@@ -255,6 +277,30 @@ def topk_order(s: np.ndarray, k: int) -> np.ndarray:
     return order[: min(k, n)]
 
 
+def block_scores(s: np.ndarray, block_len: int) -> np.ndarray:
+    """Step 7: score of key block c = max of s over its visible keys
+    [c*L, min((c+1)*L, n)); ceil(n / L) blocks."""
+    n = s.shape[0]
+    nb = -(-n // block_len)
+    return np.array([s[c * block_len:min((c + 1) * block_len, n)].max() for c in range(nb)])
+
+
+def kept_blocks(nb: int, init_num: int, local_num: int) -> np.ndarray:
+    """Step 8: the blocks always kept, ascending: the first init_num and the last
+    local_num of the nb visible blocks (each block once)."""
+    first = set(range(min(init_num, nb)))
+    last = set(range(max(nb - local_num, 0), nb))
+    return np.array(sorted(first | last), dtype=np.int64)
+
+
+def select_blocks(sb: np.ndarray, k: int, init_num: int, local_num: int) -> Tuple[np.ndarray, int]:
+    """Step 8 then step 5: (output order of block indices, number kept first)."""
+    kept = kept_blocks(sb.shape[0], init_num, local_num)
+    rest = np.setdiff1d(np.arange(sb.shape[0]), kept)
+    chosen = rest[topk_order(sb[rest], k - kept.shape[0])]
+    return np.concatenate([kept, chosen]), int(kept.shape[0])
+
+
 # ---------------------------------------------------------------------------
 # Driver
 # ---------------------------------------------------------------------------
@@ -279,7 +325,10 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
       'indices' : int32 (R, N2, k)
       'values'  : float32 (R, N2, k)
       'scores'  : (if want_scores) list over rows of lists over N2 of float64
-                  arrays holding s_j for every visible key j.
+                  arrays holding s_j for every visible key j (block scores
+                  for block_len > 1);
+      'kept'    : (if want_scores) int (R, N2): output slots taken by the
+                  blocks that are always kept (0 without init_num / local_num).
     """
     rows = list(all_rows(wl) if rows is None else rows)
     kk = wl.sparse_count
@@ -288,7 +337,9 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
     idx = np.full((R, N2, kk), -1, np.int32)
     val = np.full((R, N2, kk), -np.inf, np.float32)
     scores: List[List[np.ndarray]] = [[np.zeros(0)] * N2 for _ in range(R)]
+    kept = np.zeros((R, N2), np.int64)
     lengths = batch_lengths(wl)
+    L, init_num, local_num = routing(wl)
 
     by_batch: Dict[int, List[int]] = {}
     for r, (b, i) in enumerate(rows):
@@ -313,7 +364,11 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
                     s = row_scores(q[t, g], w[t, g], keys[:n, h],
                                    None if qs is None else qs[t, g],
                                    None if kscale is None else kscale[:n, h])
-                    order = topk_order(s, kk)
+                    if L > 1 or init_num or local_num:
+                        s = block_scores(s, L)
+                        order, kept[r, h] = select_blocks(s, kk, init_num, local_num)
+                    else:
+                        order = topk_order(s, kk)
                     m = order.shape[0]
                     idx[r, h, :m] = order + off
                     val[r, h, :m] = s[order].astype(np.float32)
@@ -322,6 +377,7 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
     out: Dict[str, object] = {"rows": rows, "indices": idx, "values": val}
     if want_scores:
         out["scores"] = scores
+        out["kept"] = kept
     return out
 
 

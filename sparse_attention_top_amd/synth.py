@@ -140,6 +140,9 @@ class Workload:
     cmp_ratio: int = 1                          # key compression ratio (1: none)
     cmp_residual_k: Optional[np.ndarray] = None  # (B,) leftover original tokens
     output_idx_offset: Optional[np.ndarray] = None  # (B,) added to returned indices
+    block_len: int = 1                          # keys per selected block (1: tokens)
+    init_num: int = 0                           # leading blocks always kept
+    local_num: int = 0                          # trailing visible blocks always kept
     seed: int = 0
     notes: Dict[str, object] = field(default_factory=dict)
 
@@ -207,7 +210,8 @@ def build(name: str, *, layout_q: str, layout_k: str, qk_dtype: str, w_dtype: st
           pass_seqused_q: Optional[bool] = None,
           pass_seqused_k: Optional[bool] = None,
           cmp_ratio: int = 1, cmp_residual_k: Optional[Sequence[int]] = None,
-          output_idx_offset: Optional[Sequence[int]] = None) -> Workload:
+          output_idx_offset: Optional[Sequence[int]] = None, block_len: int = 1,
+          init_num: int = 0, local_num: int = 0) -> Workload:
     """Draw one problem. Draw order: q, k, w, then the paged block permutation."""
     if layout_k != "PA_BSND" and layout_k != layout_q:
         raise ValueError("non-paged key layout must equal the query layout")
@@ -302,6 +306,7 @@ def build(name: str, *, layout_q: str, layout_k: str, qk_dtype: str, w_dtype: st
                                     else np.asarray(cmp_residual_k, np.int32)),
                     output_idx_offset=(None if output_idx_offset is None
                                        else np.asarray(output_idx_offset, np.int32)),
+                    block_len=int(block_len), init_num=int(init_num), local_num=int(local_num),
                     seed=seed, **wl_kw)
 
 

@@ -127,7 +127,35 @@ def check_rows(gidx_rows: np.ndarray, gval_rows: Optional[np.ndarray], oracle_ou
                 assert (g[~valid] == -1).all()
                 g = np.where(valid, g - off, g)
                 o = np.where(o >= 0, o - off, o)
-            check_row(g, None if gval_rows is None else gval_rows[r, h],
-                      oracle_out["scores"][r][h], k, tol, oidx=o, stats=st,
-                      where=f"{label} row (b={b}, i={i})")
+            gv = None if gval_rows is None else np.asarray(gval_rows[r, h], np.float64)
+            sc = oracle_out["scores"][r][h]
+            where = f"{label} row (b={b}, i={i})"
+            f = int(oracle_out["kept"][r, h]) if "kept" in oracle_out else 0
+            if f:
+                g, gv, sc, o, k_rest = _split_kept(g, gv, sc, o, f, k, tol, where)
+            else:
+                k_rest = k
+            check_row(g, gv, sc, k_rest, tol, oidx=o, stats=st, where=where)
     return st
+
+
+def _split_kept(g, gv, s, o, f, k, tol, where):
+    """Rows with blocks that are always kept: the first f slots must equal the
+    oracle's (an index rule, no scores involved), their values within the
+    tolerance; the remaining slots are then checked by the rule above over the
+    other blocks, renumbered."""
+    assert np.array_equal(g[:f], o[:f]), f"{where}: kept blocks {g[:f]} != {o[:f]}"
+    floor = 2.0 ** -6 * np.abs(s).max()
+    if gv is not None:
+        err = np.abs(gv[:f] - s[g[:f]])
+        assert (err <= tol * np.maximum(np.abs(s[g[:f]]), floor)).all(), \
+            f"{where}: kept block values off by {err.max():.3g}"
+    rest = np.setdiff1d(np.arange(s.shape[0]), g[:f])
+    pos = np.full(s.shape[0], -2, np.int64)
+    pos[rest] = np.arange(rest.shape[0])
+    def renum(x):
+        x = x[f:]
+        return np.where(x >= 0, pos[np.clip(x, 0, s.shape[0] - 1)], x)
+    gr = renum(g)
+    assert (gr != -2).all(), f"{where}: a kept block is returned twice"
+    return gr, (None if gv is None else gv[f:]), s[rest], renum(o), k - f

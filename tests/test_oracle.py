@@ -190,6 +190,9 @@ def _hand_workload(case):
                          if "cmp_residual_k" in case else None)
     ns.output_idx_offset = (np.array(case["output_idx_offset"], np.int32)
                             if "output_idx_offset" in case else None)
+    ns.block_len = case.get("block_len", 1)
+    ns.init_num = case.get("init_num", 0)
+    ns.local_num = case.get("local_num", 0)
     ns.B = 1
     ns.layout_q = "BSND"
     ns.q = _enc(qv[None], dt)
@@ -284,6 +287,45 @@ def test_brute_force_small(seed):
     assert np.allclose(s, _py_scores(q, w, keys), rtol=0, atol=1e-12)
     order = O.topk_order(s, k)
     assert list(order) == _brute_force(list(s), k)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_block_selection_brute_force(seed):
+    """Key blocks with kept sink / local blocks, against independent forms: block
+    scores by numpy's reduceat (max over each block's keys), the kept blocks as a
+    set membership test, and the rest by brute force over block subsets."""
+    rng = np.random.default_rng(2000 + seed)
+    n = int(rng.integers(1, 13))
+    L = int(rng.integers(1, 5))
+    s = rng.integers(-3, 4, n).astype(np.float64) if seed % 2 == 0 else rng.standard_normal(n)
+    sb = O.block_scores(s, L)
+    assert np.array_equal(sb, np.maximum.reduceat(s, np.arange(0, n, L)))
+    nb = sb.shape[0]
+    init_num, local_num = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+    k = int(rng.integers(max(1, init_num + local_num), nb + 3))
+    order, kept = O.select_blocks(sb, k, init_num, local_num)
+    must = [c for c in range(nb) if c < init_num or c >= nb - local_num]
+    assert kept == len(must) and list(order[:kept]) == must
+    rest = [c for c in range(nb) if c not in must]
+    best = _brute_force([sb[c] for c in rest], k - kept)
+    assert list(order[kept:]) == [rest[t] for t in best]
+    assert len(set(order.tolist())) == order.shape[0] == min(k, nb)
+
+
+def test_blocks_of_one_reduce_to_the_plain_selection():
+    """block_len 1 without kept blocks is the token top-k itself."""
+    rng = np.random.default_rng(21)
+    s = rng.integers(-4, 5, 60).astype(np.float64)
+    assert np.array_equal(O.block_scores(s, 1), s)
+    order, kept = O.select_blocks(s, 17, 0, 0)
+    assert kept == 0 and np.array_equal(order, O.topk_order(s, 17))
+
+
+def test_kept_blocks_win_over_higher_scores():
+    """Kept blocks are returned even when every other block scores higher."""
+    sb = np.array([-5.0, 9, 8, 7, 6, -4])
+    order, kept = O.select_blocks(sb, 3, 1, 1)
+    assert kept == 2 and order.tolist() == [0, 5, 1]
 
 
 # ---------------------------------------------------------------------------
