@@ -37,7 +37,11 @@
  * construction); NaN inputs give undefined rankings; with compressed keys
  * (cmp_ratio r > 1), compressed key j stands for original tokens
  * j*r .. j*r + r - 1 of a sequence of S_k*r + cmp_residual_k original tokens
- * and is visible under the right-down rule once its last token is.
+ * and is visible under the right-down rule once its last token is; with key
+ * blocks (block_len L > 1) block c holds keys c*L .. c*L + L - 1, scores the
+ * maximum over its visible keys and is visible when one of its keys is; the
+ * blocks always kept (init_num first, local_num last visible) fill the first
+ * output slots in ascending block order, the rest follow by score.
  */
 #ifndef LI_H_
 #define LI_H_
@@ -49,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LI_API_VERSION 2
+#define LI_API_VERSION 3
 
 typedef enum li_status {
   LI_OK = 0,
@@ -115,6 +119,20 @@ typedef enum li_dtype {
  *                keys) and, in sparse_mode 3, cmp_residual_k gives each
  *                sequence's leftover original tokens (row i then sees the first
  *                clamp(floor((i + 1 + S_k*r + res - S_q) / r), 0, S_k) keys).
+ *  block_len     key-block granularity of the selection (the ops-transformer
+ *                issue, LightningIndexer family: block_len 1/2/4/8/16): 0 or 1 =
+ *                single keys; 2, 4, 8, 16 = the top-k runs over blocks of that
+ *                many consecutive (compressed) keys, block score = the largest
+ *                score among the block's visible keys, output indices = block
+ *                indices (k then counts blocks).
+ *  init_num      >= 0: the first init_num visible blocks (sink tokens in the
+ *                issue's words) are always returned.
+ *  local_num     >= 0: the last local_num visible blocks of each row (the
+ *                issue's diagonal local window: under sparse_mode 3 they end at
+ *                the row's diagonal) are always returned.
+ *                init_num + local_num <= sparse_count. The blocks always kept
+ *                take the first output slots, ascending; the other slots hold
+ *                the best remaining blocks by (score desc, index asc).
  */
 typedef struct li_problem {
   uint32_t api_version;   /* LI_API_VERSION */
@@ -141,7 +159,10 @@ typedef struct li_problem {
   int64_t next_tokens;
   int32_t return_value;
   int32_t cmp_ratio;
-  int32_t reserved[6];    /* must be zero */
+  int32_t block_len;
+  int32_t init_num;
+  int32_t local_num;
+  int32_t reserved[3];    /* must be zero */
 } li_problem;
 
 /*

@@ -16,7 +16,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libli_mi355x.so")
 
-API_VERSION = 2
+API_VERSION = 3
 INT64_MAX = (1 << 63) - 1
 
 # li_status
@@ -73,7 +73,10 @@ class li_problem(ctypes.Structure):
         ("next_tokens", ctypes.c_int64),
         ("return_value", ctypes.c_int32),
         ("cmp_ratio", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 6),
+        ("block_len", ctypes.c_int32),
+        ("init_num", ctypes.c_int32),
+        ("local_num", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -103,7 +106,8 @@ def make_problem(*, layout_q="BSND", layout_k="BSND", dtype_qk="bf16", dtype_w="
                  dtype_scale="f32", batch=1, s1=0, s2=0, n1=64, n2=1, d=128, t1=0, t2=0,
                  block_size=0, max_blocks_per_seq=0, num_blocks=0, k_block_stride=0,
                  sparse_count=2048, sparse_mode=3, pre_tokens=INT64_MAX,
-                 next_tokens=INT64_MAX, return_value=False, cmp_ratio=1) -> li_problem:
+                 next_tokens=INT64_MAX, return_value=False, cmp_ratio=1, block_len=1,
+                 init_num=0, local_num=0) -> li_problem:
     p = li_problem()
     p.api_version = API_VERSION
     p.layout_q = LAYOUTS[layout_q] if isinstance(layout_q, str) else int(layout_q)
@@ -120,6 +124,8 @@ def make_problem(*, layout_q="BSND", layout_k="BSND", dtype_qk="bf16", dtype_w="
     p.pre_tokens, p.next_tokens = int(pre_tokens), int(next_tokens)
     p.return_value = int(bool(return_value))
     p.cmp_ratio = int(cmp_ratio)
+    p.block_len = int(block_len)
+    p.init_num, p.local_num = int(init_num), int(local_num)
     return p
 
 

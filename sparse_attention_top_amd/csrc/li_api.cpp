@@ -115,6 +115,14 @@ li_status check_problem(const li_problem* p) {
            "cmp_ratio must be in [0, 128] (0 and 1 mean uncompressed keys), got %d", p->cmp_ratio);
   LI_CHECK(p->sparse_mode == 0 || p->sparse_mode == 3, LI_ERR_INVALID_ARGUMENT,
            "sparse_mode must be 0 or 3 (got %d)", p->sparse_mode);
+  LI_CHECK(p->block_len == 0 || p->block_len == 1 || p->block_len == 2 || p->block_len == 4 ||
+               p->block_len == 8 || p->block_len == 16,
+           LI_ERR_INVALID_ARGUMENT, "block_len must be 0, 1, 2, 4, 8 or 16 (got %d)", p->block_len);
+  LI_CHECK(p->init_num >= 0 && p->local_num >= 0, LI_ERR_INVALID_ARGUMENT,
+           "init_num and local_num must be non-negative");
+  LI_CHECK((int64_t)p->init_num + p->local_num <= p->sparse_count, LI_ERR_INVALID_ARGUMENT,
+           "init_num + local_num (%d + %d) exceeds sparse_count %d", p->init_num, p->local_num,
+           p->sparse_count);
   LI_CHECK(p->pre_tokens == kInt64Max && p->next_tokens == kInt64Max, LI_ERR_UNSUPPORTED,
            "pre_tokens / next_tokens support only their default 2^63-1");
   LI_CHECK(p->return_value == 0 || p->return_value == 1, LI_ERR_INVALID_ARGUMENT,
@@ -123,12 +131,13 @@ li_status check_problem(const li_problem* p) {
 }
 
 int32_t cmp_ratio_of(const li_problem& p) { return p.cmp_ratio > 1 ? p.cmp_ratio : 1; }
+int32_t block_len_of(const li_problem& p) { return p.block_len > 1 ? p.block_len : 1; }
 
 uint64_t problem_hash(const li_problem& p) {
   // FNV-1a over the fields that shape the work decomposition.
   const int64_t f[] = {p.layout_q, p.layout_k, p.dtype_qk, p.batch, p.s1, p.s2, p.n1, p.n2, p.d,
                        p.t1, p.t2, p.block_size, p.max_blocks_per_seq, p.num_blocks,
-                       p.sparse_mode, cmp_ratio_of(p)};
+                       p.sparse_mode, cmp_ratio_of(p), block_len_of(p)};
   uint64_t h = 1469598103934665603ull;
   const unsigned char* b = reinterpret_cast<const unsigned char*>(f);
   for (size_t i = 0; i < sizeof f; ++i) {
@@ -292,6 +301,10 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     auto visible = [&](int b, int i) {
       return visible_keys(i, sq[b], sk[b], p->sparse_mode, cr, cres[b]);
     };
+    // Rows select over blocks of bl keys when block_len > 1: one stored score
+    // per block.
+    const int32_t bl = block_len_of(*p);
+    auto blocks = [&](int n) { return (n + bl - 1) / bl; };
 
     // ---- variant and tiling ----
     int max_sq = 0, max_sk = 0;
@@ -329,7 +342,7 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
       r.k_base = k_base[b];
       r.s_q = sq[b];
       r.s_k = sk[b];
-      r.ld = std::max(4, (sk[b] + 3) / 4 * 4);
+      r.ld = std::max(4, (blocks(sk[b]) + 3) / 4 * 4);
       r.rows = rows[b];
       r.cmp_res = cres[b];
       r.reserved = 0;
@@ -368,7 +381,7 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     int64_t covered = 0;
     for (int b = 0; b < B; ++b) {
       for (int i = 0; i < rows[b]; ++i) {
-        const int n = i < sq[b] ? visible(b, i) : 0;
+        const int n = i < sq[b] ? blocks(visible(b, i)) : 0;
         const int64_t off = n > 0 ? recs[b].ws_off + (int64_t)i * recs[b].ld : 0;
         by_class[topk_class(n)].push_back({off, (int32_t)(row_base[b] + i), n, ioff[b], 0});
       }
@@ -486,6 +499,9 @@ li_status li_score(const li_problem* p, const li_inputs* in, const void* meta_ho
   a.max_blocks = p->max_blocks_per_seq;
   a.sparse_mode = p->sparse_mode;
   a.cmp_ratio = cmp_ratio_of(*p);
+  a.key_block = block_len_of(*p);
+  a.key_block_shift = 0;
+  while ((1 << a.key_block_shift) < a.key_block) ++a.key_block_shift;
   const hipError_t e = launch_score(*p, h->variant, h->num_items, a, (hipStream_t)stream);
   LI_CHECK(e == hipSuccess, LI_ERR_HIP, "score kernel launch: %s", hipGetErrorString(e));
   return LI_OK;
@@ -514,6 +530,8 @@ li_status li_topk(const li_problem* p, const void* meta_host, const void* meta_d
   a.out_idx = sparse_indices;
   a.out_val = p->return_value ? sparse_values : nullptr;
   a.k = p->sparse_count;
+  a.init_num = p->init_num;
+  a.local_num = p->local_num;
   for (int c = 0; c <= kTopkClasses; ++c) a.row_class[c] = h->row_class[c];
   const hipError_t e = launch_topk(*p, a, (hipStream_t)stream);
   LI_CHECK(e == hipSuccess, LI_ERR_HIP, "top-k kernel launch: %s", hipGetErrorString(e));

@@ -25,7 +25,7 @@ namespace li {
 // count and workspace offset so that a top-k workgroup needs one record.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMetaMagic = 0x444D494Cu;  // "LIMD"
-constexpr uint32_t kMetaVersion = 3;
+constexpr uint32_t kMetaVersion = 4;
 
 // Top-k size classes: class c holds the rows of at most kTopkClassKeys[c]
 // visible keys (the last class is unbounded) and runs with kTopkClassThreads[c]
@@ -82,7 +82,8 @@ static_assert(sizeof(WorkItem) == 16, "work item size");
 struct RowRec {
   int64_t ws_off;      // first workspace float of the row's scores
   int32_t row;         // output row (B*S1 rows for BSND, T1 for TND)
-  int32_t n;           // visible keys (0 for rows past a sequence's actual length)
+  int32_t n;           // visible keys, or visible key blocks when block_len > 1
+                       // (0 for rows past a sequence's actual length)
   int32_t idx_offset;  // added to every returned index (output_idx_offset)
   int32_t reserved;
 };
@@ -121,6 +122,8 @@ struct ScoreArgs {
   int32_t max_blocks;
   int32_t sparse_mode;
   int32_t cmp_ratio;       // 1 for uncompressed keys
+  int32_t key_block;       // keys per stored score (block_len; 1: one score per key)
+  int32_t key_block_shift; // log2(key_block)
 };
 
 struct TopkArgs {
@@ -129,6 +132,8 @@ struct TopkArgs {
   int32_t* out_idx;
   float* out_val;          // may be null
   int32_t k;
+  int32_t init_num;        // leading blocks of every row that are always returned
+  int32_t local_num;       // trailing visible blocks of every row that are always returned
   int32_t row_class[kTopkClasses + 1];   // class boundaries in rows (host copy)
 };
 

@@ -142,13 +142,31 @@ __device__ inline void lds_dma16(const void* gptr, uint32_t lds) {
                : "memory", "m0");
 }
 
+// v from the lane that a DPP permutation inside 16-lane rows selects.
+template <int CTRL> __device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over aligned groups of `len` consecutive lanes (len in 1..16, a power of
+// two): xor-1 and xor-2 quad permutations, then the half-row and row mirrors,
+// which pair the two halves of each 8- and 16-lane group.
+__device__ inline float group_max(float v, int len) {
+  if (len >= 2) v = fmaxf(v, dpp<0xB1>(v));     // quad_perm [1,0,3,2]
+  if (len >= 4) v = fmaxf(v, dpp<0x4E>(v));     // quad_perm [2,3,0,1]
+  if (len >= 8) v = fmaxf(v, dpp<0x141>(v));    // row_half_mirror
+  if (len >= 16) v = fmaxf(v, dpp<0x140>(v));   // row_mirror
+  return v;
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // and all its LDS operations are done, then barrier the workgroup.
 template <int N> __device__ inline void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <int DT, int D, int NT, int WQ, int WK, int KT>
+// BL: store one score per block of block_len keys (the block maximum) instead
+// of one per key.
+template <int DT, int D, int NT, int WQ, int WK, int KT, bool BL>
 __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
   using M = Mma<DT>;
   using Frag = typename M::Frag;
@@ -197,8 +215,11 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
   const int lim = nv < it.k1 ? nv : it.k1;   // this row stores keys [k0, lim)
   const int64_t qrow = (int64_t)br.row_base + (row_ok ? row : 0);
   float* out_row = a.ws + br.ws_off + (int64_t)(row_ok ? row : 0) * br.ld;
-  const auto out_rsrc = __builtin_amdgcn_make_buffer_rsrc(out_row, (short)0, lim > 0 ? lim * 4 : 0,
-                                                          kRsrcWord3);
+  // Stored floats of the row: keys [0, lim), or the blocks holding them. Items
+  // start at multiples of KT, so no block straddles two items.
+  const int nstore = BL ? (lim + a.key_block - 1) >> a.key_block_shift : lim;
+  const auto out_rsrc = __builtin_amdgcn_make_buffer_rsrc(out_row, (short)0,
+                                                          nstore > 0 ? nstore * 4 : 0, kRsrcWord3);
 
   // Key staging. Stage st covers keys [k0 + st*KT, k0 + (st+1)*KT); keys past
   // k1 are clamped to the item's last key (computed, never stored), so every
@@ -401,12 +422,23 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
   // Cross-half swap-add (both halves end up with the full sum over heads) and
   // the store of the slice starting at key kb by the lower half-wave; keys at
   // or past the row's limit fall outside the buffer record and are dropped.
+  // With blocks, keys past the limit count as -inf in their block's maximum
+  // and the first lane of each block stores it.
   auto finish = [&](float part, int kb, float ks, bool valid) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
                                                      __float_as_uint(part), false, false);
-    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int off = (half == 0 && valid) ? (kb + col) * 4 : kDropOffset;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(QUANT ? tot * ks : tot), out_rsrc, off, 0, 0);
+    float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (QUANT) tot *= ks;
+    int off;
+    if constexpr (BL) {
+      const int j = kb + col;
+      tot = group_max(j < lim ? tot : -__builtin_huge_valf(), a.key_block);
+      off = (half == 0 && valid && (col & (a.key_block - 1)) == 0) ? (j >> a.key_block_shift) * 4
+                                                                    : kDropOffset;
+    } else {
+      off = (half == 0 && valid) ? (kb + col) * 4 : kDropOffset;
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rsrc, off, 0, 0);
   };
 
   Acc acc0[NT], acc1[NT];   // even slices of a stage accumulate in acc0, odd in acc1
@@ -436,20 +468,20 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
   finish(epi(acc1), slice_key(nstages - 1, SPS - 1), ks1, true);
 }
 
-template <int DT, int D, int NT>
+template <int DT, int D, int NT, bool BL>
 hipError_t launch_v(int variant, int num_items, const ScoreArgs& a, hipStream_t s) {
   switch (variant) {
     case kVarPrefill:
-      hipLaunchKernelGGL((score_kernel<DT, D, NT, 8, 1, kVariantTileK[kVarPrefill]>), dim3(num_items),
-                         dim3(512), 0, s, a);
+      hipLaunchKernelGGL((score_kernel<DT, D, NT, 8, 1, kVariantTileK[kVarPrefill], BL>),
+                         dim3(num_items), dim3(512), 0, s, a);
       break;
     case kVarMid:
-      hipLaunchKernelGGL((score_kernel<DT, D, NT, 4, 2, kVariantTileK[kVarMid]>), dim3(num_items),
-                         dim3(512), 0, s, a);
+      hipLaunchKernelGGL((score_kernel<DT, D, NT, 4, 2, kVariantTileK[kVarMid], BL>),
+                         dim3(num_items), dim3(512), 0, s, a);
       break;
     case kVarDecode:
-      hipLaunchKernelGGL((score_kernel<DT, D, NT, 2, 4, kVariantTileK[kVarDecode]>), dim3(num_items),
-                         dim3(512), 0, s, a);
+      hipLaunchKernelGGL((score_kernel<DT, D, NT, 2, 4, kVariantTileK[kVarDecode], BL>),
+                         dim3(num_items), dim3(512), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;
@@ -457,13 +489,20 @@ hipError_t launch_v(int variant, int num_items, const ScoreArgs& a, hipStream_t 
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool BL>
 hipError_t launch_dt(int d, int nt, int variant, int num_items, const ScoreArgs& a, hipStream_t s) {
-  if (d == 128) return nt == 1 ? launch_v<DT, 128, 1>(variant, num_items, a, s)
-                               : launch_v<DT, 128, 2>(variant, num_items, a, s);
-  if (d == 64) return nt == 1 ? launch_v<DT, 64, 1>(variant, num_items, a, s)
-                              : launch_v<DT, 64, 2>(variant, num_items, a, s);
+  if (d == 128) return nt == 1 ? launch_v<DT, 128, 1, BL>(variant, num_items, a, s)
+                               : launch_v<DT, 128, 2, BL>(variant, num_items, a, s);
+  if (d == 64) return nt == 1 ? launch_v<DT, 64, 1, BL>(variant, num_items, a, s)
+                              : launch_v<DT, 64, 2, BL>(variant, num_items, a, s);
   return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t launch_blk(const ScoreArgs& a, int d, int nt, int variant, int num_items,
+                      hipStream_t s) {
+  return a.key_block > 1 ? launch_dt<DT, true>(d, nt, variant, num_items, a, s)
+                         : launch_dt<DT, false>(d, nt, variant, num_items, a, s);
 }
 
 }  // namespace
@@ -473,10 +512,10 @@ hipError_t launch_score(const li_problem& p, int variant, int num_items, const S
   if (num_items <= 0) return hipSuccess;
   const int nt = p.n1 > 32 ? 2 : 1;
   switch (p.dtype_qk) {
-    case LI_DTYPE_BF16: return launch_dt<LI_DTYPE_BF16>(p.d, nt, variant, num_items, a, s);
-    case LI_DTYPE_F16: return launch_dt<LI_DTYPE_F16>(p.d, nt, variant, num_items, a, s);
-    case LI_DTYPE_E4M3FN: return launch_dt<LI_DTYPE_E4M3FN>(p.d, nt, variant, num_items, a, s);
-    case LI_DTYPE_I8: return launch_dt<LI_DTYPE_I8>(p.d, nt, variant, num_items, a, s);
+    case LI_DTYPE_BF16: return launch_blk<LI_DTYPE_BF16>(a, p.d, nt, variant, num_items, s);
+    case LI_DTYPE_F16: return launch_blk<LI_DTYPE_F16>(a, p.d, nt, variant, num_items, s);
+    case LI_DTYPE_E4M3FN: return launch_blk<LI_DTYPE_E4M3FN>(a, p.d, nt, variant, num_items, s);
+    case LI_DTYPE_I8: return launch_blk<LI_DTYPE_I8>(a, p.d, nt, variant, num_items, s);
     default: return hipErrorInvalidValue;
   }
 }

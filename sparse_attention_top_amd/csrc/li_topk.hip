@@ -157,15 +157,29 @@ struct Bucketing {
   }
 };
 
-// The row's n scores. RES: in registers, thread t holding the float4 groups
-// t + NT*v (v < R/4), i.e. key 4*(t + NT*v) + e in x[4v + e]. Otherwise they
-// are streamed from memory on every pass, with the same key-to-thread map.
-template <int NT, int R, bool RES>
+// Which keys of a float4 group starting at key j0 take part: e in [beg, end)
+// (beg = lo - j0; it matters only when leading keys are left out, KEPT).
+template <bool KEPT>
+struct GroupRange {
+  int beg, end;
+  __device__ bool ok(int e) const { return (!KEPT || e >= beg) && e < end; }
+};
+
+// The row's scores; keys [lo, n) take part in the selection (lo > 0 only with
+// KEPT, when the leading blocks are always kept and so left out). RES: in
+// registers, thread t holding the float4 groups t + NT*v (v < R/4), i.e. key
+// 4*(t + NT*v) + e in x[4v + e]. Otherwise they are streamed from memory on
+// every pass, with the same key-to-thread map.
+template <int NT, int R, bool RES, bool KEPT>
 struct Row {
   static_assert(R % 4 == 0, "whole float4 groups per thread");
   const float* src;   // 16-byte aligned, readable up to the float4 group holding key n-1
   int n;
+  int lo_;
   float x[RES ? R : 4];
+
+  __device__ int lo() const { return KEPT ? lo_ : 0; }
+  __device__ int count() const { return n - lo(); }
 
   __device__ inline float4 group(int v) const {   // float4 group v, clamped in range
     const int last = (n - 1) >> 2;
@@ -186,8 +200,8 @@ struct Row {
     }
   }
 
-  // f(x[4], first key, keys of the group below n) for every float4 group that
-  // holds keys < n.
+  // f(x[4], first key, GroupRange) for every float4 group that holds keys in
+  // [lo, n).
   template <typename F>
   __device__ inline void each4(F&& f) const {
     if constexpr (RES) {
@@ -196,7 +210,7 @@ struct Row {
         if (4 * NT * v >= n) break;   // uniform
         const int j0 = 4 * (threadIdx.x + NT * v);
         const float g[4] = {x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
-        if (j0 < n) f(g, j0, min(4, n - j0));
+        if (j0 < n && (!KEPT || j0 + 4 > lo_)) f(g, j0, GroupRange<KEPT>{lo() - j0, n - j0});
       }
     } else {
       constexpr int kBatch = 4;   // float4 groups in flight per thread
@@ -208,14 +222,14 @@ struct Row {
         for (int u = 0; u < kBatch; ++u) {
           const int j0 = 4 * (v0 + u * NT);
           const float g[4] = {canon(q[u].x), canon(q[u].y), canon(q[u].z), canon(q[u].w)};
-          if (j0 < n) f(g, j0, min(4, n - j0));
+          if (j0 < n && (!KEPT || j0 + 4 > lo_)) f(g, j0, GroupRange<KEPT>{lo() - j0, n - j0});
         }
       }
     }
   }
 
-  // f(score, key) for every key < n. Groups that lie wholly below n (known for
-  // the whole block) skip the per-key bound test.
+  // f(score, key) for every key in [lo, n). Groups that lie wholly inside
+  // (known for the whole block) skip the per-key bound test.
   template <typename F>
   __device__ inline void each(F&& f) const {
     if constexpr (RES) {
@@ -223,13 +237,13 @@ struct Row {
       for (int v = 0; v < R / 4; ++v) {
         if (4 * NT * v >= n) break;   // uniform
         const int j0 = 4 * (threadIdx.x + NT * v);
-        if (4 * NT * (v + 1) <= n) {  // uniform
+        if ((!KEPT || 4 * NT * v >= lo_) && 4 * NT * (v + 1) <= n) {  // uniform
 #pragma unroll
           for (int e = 0; e < 4; ++e) f(x[4 * v + e], j0 + e);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (j0 + e < n) f(x[4 * v + e], j0 + e);
+            if ((!KEPT || j0 + e >= lo_) && j0 + e < n) f(x[4 * v + e], j0 + e);
         }
       }
     } else {
@@ -244,7 +258,7 @@ struct Row {
           const float s[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (j0 + e < n) f(canon(s[e]), j0 + e);
+            if ((!KEPT || j0 + e >= lo_) && j0 + e < n) f(canon(s[e]), j0 + e);
         }
       }
     }
@@ -261,11 +275,11 @@ __device__ inline void fill_tail(int m, int K, int32_t* oi, float* ov, int nt) {
 
 // Fast path; returns false (before writing any output) if it cannot handle the row.
 // The histogram words must be zero on entry.
-template <int NT, int R, bool RES, bool W16, int KMAX>
-__device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi, int K, int m,
+template <int NT, int R, bool RES, bool KEPT, bool W16, int KMAX>
+__device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, float hi, int K, int m,
                                   int32_t* oi, float* ov, int32_t ioff, Smem<NT, W16, KMAX>& sm) {
   const int tid = threadIdx.x;
-  const int n = row.n;
+  const int n = row.count();
   const float range = hi - lo;
   if (!(hi > lo) || !(range <= 3.0e38f)) return false;
   const float scale = (float)kBuckets / range;
@@ -347,17 +361,17 @@ __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi
 
   // Counting sort of the keys of buckets >= t into their bucket segments.
   // Afterwards bucket b's segment is [end(b+1), end(b)) (end(kBuckets) = 0).
-  row.each4([&](const float (&x)[4], int j0, int valid) {
+  row.each4([&](const float (&x)[4], int j0, auto rng) {
     int b[4];
     uint32_t pos[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {   // all four fetch-adds in flight before any write
       b[e] = bucket(x[e]);
-      if (e < valid && b[e] >= t) pos[e] = cnt.fetch_add(b[e]);
+      if (rng.ok(e) && b[e] >= t) pos[e] = cnt.fetch_add(b[e]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (e < valid && b[e] >= t) sm.buf[pos[e]] = composite(x[e], j0 + e);
+      if (rng.ok(e) && b[e] >= t) sm.buf[pos[e]] = composite(x[e], j0 + e);
   });
   __syncthreads();
   const uint32_t ncand = cnt.get(t);
@@ -412,16 +426,16 @@ __device__ bool select_by_buckets(const Row<NT, R, RES>& row, float lo, float hi
 }
 
 // Fallback: exact radix select over the composite, then bitonic sort.
-template <int NT, int R, bool RES, bool W16, int KMAX>
-__device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_t* oi, float* ov,
+template <int NT, int R, bool RES, bool KEPT, bool W16, int KMAX>
+__device__ void select_by_radix(const Row<NT, R, RES, KEPT>& row, int K, int m, int32_t* oi, float* ov,
                                 int32_t ioff, Smem<NT, W16, KMAX>& sm) {
   const int tid = threadIdx.x;
-  const int n = row.n;
+  const int n = row.count();
   uint32_t* cnt = sm.cnt;   // kRadixBins 32-bit counters
   int P = 1;
   while (P < m) P <<= 1;
   if (n <= K) {
-    row.each([&](float x, int j) { sm.buf[j] = composite(x, j); });
+    row.each([&](float x, int j) { sm.buf[j - row.lo()] = composite(x, j); });
     for (int j = n + tid; j < P; j += NT) sm.buf[j] = 0ull;
   } else {
     const int kShift[6] = {53, 42, 32, 21, 10, 0};
@@ -511,23 +525,43 @@ __device__ void select_by_radix(const Row<NT, R, RES>& row, int K, int m, int32_
 // comes from rows in flight: the 256-thread kernels are held to the register
 // budget of five (8K-key rows) or six (shorter rows) workgroups per CU, six
 // being also what the LDS allows.
-template <int NT, int R, bool RES, bool W16, int KMAX>
+template <int NT, int R, bool RES, bool KEPT, bool W16, int KMAX>
 __global__ __launch_bounds__(NT, (NT == 256 && KMAX == kMaxKSmall) ? (R == 32 ? 5 : 6) : 1)
 void topk_kernel(TopkArgs a, int first) {
   __shared__ Smem<NT, W16, KMAX> sm;
   const RowRec rr = a.rows[first + blockIdx.x];
-  const int n = rr.n;
-  const int K = a.k;
+  const int nb = rr.n;
+  int32_t* oi = a.out_idx + (int64_t)rr.row * a.k;
+  float* ov = a.out_val ? a.out_val + (int64_t)rr.row * a.k : nullptr;
+  const float* src = a.ws + rr.ws_off;
+  int K = a.k;
+  Row<NT, R, RES, KEPT> row;
+  row.src = src;
+  row.n = nb;
+  row.lo_ = 0;
+  if constexpr (KEPT) {
+    // Blocks always kept: [0, a1) and [b0, nb). They take the first output
+    // slots in ascending order; the selection runs over [a1, b0) for the rest.
+    const int a1 = min(a.init_num, nb);
+    const int b0 = max(a1, nb - a.local_num);
+    const int kept = a1 + (nb - b0);
+    for (int e = threadIdx.x; e < kept; e += NT) {
+      const int j = e < a1 ? e : b0 + (e - a1);
+      oi[e] = j + rr.idx_offset;
+      if (ov) ov[e] = canon(src[j]);
+    }
+    oi += kept;
+    if (ov) ov += kept;
+    K -= kept;
+    row.n = b0;
+    row.lo_ = a1;
+  }
+  const int n = row.count();
   const int m = n < K ? n : K;
-  int32_t* oi = a.out_idx + (int64_t)rr.row * K;
-  float* ov = a.out_val ? a.out_val + (int64_t)rr.row * K : nullptr;
-  if (n == 0) {
+  if (m == 0) {
     fill_tail(0, K, oi, ov, NT);
     return;
   }
-  Row<NT, R, RES> row;
-  row.src = a.ws + rr.ws_off;
-  row.n = n;
   row.load();
   // Clear the histogram while the row loads.
   for (int w = threadIdx.x; w < (int)(sizeof(sm.cnt) / 4); w += NT) sm.cnt[w] = 0u;
@@ -539,33 +573,38 @@ void topk_kernel(TopkArgs a, int first) {
   });
   block_minmax<NT>(lo, hi, sm.s_red);
   const bool fast = (!W16 || n <= 65535) &&
-                    select_by_buckets<NT, R, RES, W16, KMAX>(row, lo, hi, K, m, oi, ov,
-                                                             rr.idx_offset, sm);
+                    select_by_buckets<NT, R, RES, KEPT, W16, KMAX>(row, lo, hi, K, m, oi, ov,
+                                                                   rr.idx_offset, sm);
   if (!fast) {
     __syncthreads();
-    select_by_radix<NT, R, RES, W16, KMAX>(row, K, m, oi, ov, rr.idx_offset, sm);
+    select_by_radix<NT, R, RES, KEPT, W16, KMAX>(row, K, m, oi, ov, rr.idx_offset, sm);
   }
 }
 
-template <int NT, int R, bool RES, bool W16, int KMAX>
+template <int NT, int R, bool RES, bool W16, int KMAX, bool KEPT>
 hipError_t launch_class(const TopkArgs& a, int c, hipStream_t s) {
   const int first = a.row_class[c];
   const int count = a.row_class[c + 1] - first;
   if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL((topk_kernel<NT, R, RES, W16, KMAX>), dim3((unsigned)count), dim3(NT), 0, s,
-                     a, first);
+  hipLaunchKernelGGL((topk_kernel<NT, R, RES, KEPT, W16, KMAX>), dim3((unsigned)count), dim3(NT),
+                     0, s, a, first);
   return hipGetLastError();
 }
 
-template <int KMAX>
+template <int KMAX, bool KEPT>
 hipError_t launch_all(const TopkArgs& a, hipStream_t s) {
   hipError_t e;
-  if ((e = launch_class<256, 8, true, true, KMAX>(a, 0, s)) != hipSuccess) return e;
-  if ((e = launch_class<256, 16, true, true, KMAX>(a, 1, s)) != hipSuccess) return e;
-  if ((e = launch_class<256, 32, true, true, KMAX>(a, 2, s)) != hipSuccess) return e;
-  if ((e = launch_class<512, 32, true, true, KMAX>(a, 3, s)) != hipSuccess) return e;
-  if ((e = launch_class<1024, 32, true, true, KMAX>(a, 4, s)) != hipSuccess) return e;
-  return launch_class<1024, 4, false, false, KMAX>(a, 5, s);
+  if ((e = launch_class<256, 8, true, true, KMAX, KEPT>(a, 0, s)) != hipSuccess) return e;
+  if ((e = launch_class<256, 16, true, true, KMAX, KEPT>(a, 1, s)) != hipSuccess) return e;
+  if ((e = launch_class<256, 32, true, true, KMAX, KEPT>(a, 2, s)) != hipSuccess) return e;
+  if ((e = launch_class<512, 32, true, true, KMAX, KEPT>(a, 3, s)) != hipSuccess) return e;
+  if ((e = launch_class<1024, 32, true, true, KMAX, KEPT>(a, 4, s)) != hipSuccess) return e;
+  return launch_class<1024, 4, false, false, KMAX, KEPT>(a, 5, s);
+}
+
+template <bool KEPT>
+hipError_t launch_k(const TopkArgs& a, hipStream_t s) {
+  return a.k <= kMaxKSmall ? launch_all<kMaxKSmall, KEPT>(a, s) : launch_all<kMaxKLarge, KEPT>(a, s);
 }
 
 }  // namespace
@@ -581,7 +620,7 @@ hipError_t launch_topk(const li_problem& p, const TopkArgs& a, hipStream_t s) {
   static_assert(kTopkClassThreads[0] == 256 && kTopkClassThreads[3] == 512 &&
                     kTopkClassThreads[4] == 1024 && kTopkClassThreads[5] == 1024,
                 "class thread counts");
-  return a.k <= kMaxKSmall ? launch_all<kMaxKSmall>(a, s) : launch_all<kMaxKLarge>(a, s);
+  return (a.init_num > 0 || a.local_num > 0) ? launch_k<true>(a, s) : launch_k<false>(a, s);
 }
 
 }  // namespace li

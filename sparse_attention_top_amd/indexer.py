@@ -8,7 +8,9 @@ lengths for BSND and PA_BSND, and prefix sums without the leading zero for
 TND; ``sparse_values`` comes back with shape (0,) when ``return_value`` is
 False (CANN V2 guide, return value section). The V2 guide's compressed keys
 (``cmp_ratio``, ``cmp_residual_k``) and per-batch ``output_idx_offset`` are
-accepted as keywords too.
+accepted as keywords too, and so are the key-block routing options the
+ops-transformer issue lists for the forward operator (``block_len``,
+``init_num``, ``local_num``).
 """
 from __future__ import annotations
 
@@ -76,6 +78,7 @@ def lightning_indexer(query: torch.Tensor, key: torch.Tensor, weights: torch.Ten
                       query_dequant_scale: Optional[torch.Tensor] = None,
                       key_dequant_scale: Optional[torch.Tensor] = None,
                       cmp_ratio: int = 1, cmp_residual_k=None, output_idx_offset=None,
+                      block_len: int = 1, init_num: int = 0, local_num: int = 0,
                       plan: Optional[Plan] = None, num_cus: int = 256):
     """Top-k key indices (int32) and optionally values (float32) per query token."""
     dev = query.device
@@ -103,7 +106,8 @@ def lightning_indexer(query: torch.Tensor, key: torch.Tensor, weights: torch.Ten
     kw = dict(layout_q=layout_query, layout_k=layout_key, dtype_qk=dt,
               dtype_w=_W_DTYPES[weights.dtype], n1=n1, d=d, sparse_count=sparse_count,
               sparse_mode=sparse_mode, pre_tokens=pre_tokens, next_tokens=next_tokens,
-              return_value=return_value, cmp_ratio=cmp_ratio)
+              return_value=return_value, cmp_ratio=cmp_ratio, block_len=block_len,
+              init_num=init_num, local_num=local_num)
     aq = _host_i32(actual_seq_lengths_query)
     ak = _host_i32(actual_seq_lengths_key)
     cu_q = cu_k = used_q = used_k = None
@@ -184,7 +188,8 @@ def problem_of(wl, return_value: Optional[bool] = None) -> B.li_problem:
     kw = dict(layout_q=wl.layout_q, layout_k=wl.layout_k, dtype_qk=wl.qk_dtype,
               dtype_w=wl.w_dtype, batch=wl.B, n1=wl.N1, n2=wl.N2, d=wl.D,
               sparse_count=wl.sparse_count, sparse_mode=wl.sparse_mode, return_value=rv,
-              cmp_ratio=getattr(wl, "cmp_ratio", 1))
+              cmp_ratio=getattr(wl, "cmp_ratio", 1), block_len=getattr(wl, "block_len", 1),
+              init_num=getattr(wl, "init_num", 0), local_num=getattr(wl, "local_num", 0))
     if wl.layout_q == "TND":
         kw["t1"] = int(wl.q.shape[0])
     else:

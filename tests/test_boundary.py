@@ -65,6 +65,12 @@ BAD = [
     ("k too big", dict(sparse_count=8193), B.ERR_INVALID_ARGUMENT),
     ("cmp ratio negative", dict(cmp_ratio=-1), B.ERR_INVALID_ARGUMENT),
     ("cmp ratio too big", dict(cmp_ratio=129), B.ERR_INVALID_ARGUMENT),
+    ("block_len 3", dict(block_len=3), B.ERR_INVALID_ARGUMENT),
+    ("block_len 32", dict(block_len=32), B.ERR_INVALID_ARGUMENT),
+    ("block_len negative", dict(block_len=-2), B.ERR_INVALID_ARGUMENT),
+    ("init_num negative", dict(init_num=-1), B.ERR_INVALID_ARGUMENT),
+    ("local_num negative", dict(local_num=-1), B.ERR_INVALID_ARGUMENT),
+    ("kept blocks above k", dict(sparse_count=8, init_num=5, local_num=4), B.ERR_INVALID_ARGUMENT),
     ("mode 1", dict(sparse_mode=1), B.ERR_INVALID_ARGUMENT),
     ("mode 2", dict(sparse_mode=2), B.ERR_INVALID_ARGUMENT),
     ("pre_tokens", dict(pre_tokens=100), B.ERR_UNSUPPORTED),
@@ -94,7 +100,7 @@ def test_problem_checks(lib, name, kw, status):
 
 def test_reserved_and_version(lib):
     p = _prob()
-    p.reserved[3] = 1
+    p.reserved[2] = 1
     assert _status(p) == B.ERR_INVALID_ARGUMENT
     p = _prob()
     p.api_version = 99
@@ -216,6 +222,12 @@ WORKLOADS = {
                                       seqlens_k=[80, 3, 20], S1=300, S2=80, sparse_count=32,
                                       sparse_mode=3, cmp_ratio=4, cmp_residual_k=[3, 0, 1],
                                       output_idx_offset=[0, 1000, 77], seed=7),
+    # key blocks of 16 over compressed keys, with sink and local blocks
+    "blocks": lambda: synth.build("bl", layout_q="TND", layout_k="TND", qk_dtype="bf16",
+                                  w_dtype="f32", N1=8, D=64, seqlens_q=[40, 3, 0, 9],
+                                  seqlens_k=[500, 70, 5, 33], sparse_count=16, sparse_mode=3,
+                                  cmp_ratio=2, cmp_residual_k=[1, 0, 1, 1], block_len=16,
+                                  init_num=2, local_num=3, seed=10),
     "compressed_tnd": lambda: synth.build("zt", layout_q="TND", layout_k="TND",
                                           qk_dtype="e4m3fn", w_dtype="f32", N1=32, D=128,
                                           seqlens_q=[128, 1, 50], seqlens_k=[1000, 9, 13],
@@ -255,7 +267,8 @@ def _row_table(wl, meta):
         for rec in rows[bounds[c]:bounds[c + 1]]:
             row = int(rec["row"])
             b, i = where[row]
-            n = visible(wl, b, i) if i < int(wl.seqlens_q[b]) else 0
+            L = max(1, wl.block_len)
+            n = -(-visible(wl, b, i) // L) if i < int(wl.seqlens_q[b]) else 0
             assert int(rec["n"]) == n
             off = 0 if wl.output_idx_offset is None else int(wl.output_idx_offset[b])
             assert int(rec["idx_offset"]) == off
@@ -275,8 +288,9 @@ def test_metadata_covers_every_pair_once(lib, name):
     _row_table(wl, meta)
     assert int(h["num_rows"]) == wl.num_rows
     # workspace rows are 16-byte aligned and long enough
+    L = max(1, wl.block_len)
     for b in range(wl.B):
-        assert int(recs[b]["ld"]) % 4 == 0 and int(recs[b]["ld"]) >= int(recs[b]["s_k"])
+        assert int(recs[b]["ld"]) % 4 == 0 and int(recs[b]["ld"]) >= -(-int(recs[b]["s_k"]) // L)
         assert int(recs[b]["ws_off"]) % 4 == 0
     assert B.li_workspace_size(dp, meta) >= 4 * int(sum(int(r["s_q"]) * int(r["ld"])
                                                         for r in recs))

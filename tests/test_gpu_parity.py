@@ -161,6 +161,32 @@ EDGE = {
                           N1=8, D=64, seqlens_q=[1, 2, 1, 1, 2, 1],
                           seqlens_k=[100, 3000, 8192, 9000, 20000, 40000], sparse_count=8192,
                           sparse_mode=0),
+    # key blocks (block maximum stored by the score kernel) and kept sink / local blocks
+    "blocks_l2_local": dict(layout_q="BSND", layout_k="BSND", qk_dtype="bf16", w_dtype="bf16",
+                            N1=64, D=128, seqlens_q=[300], seqlens_k=[2000], sparse_count=256,
+                            sparse_mode=3, block_len=2, local_num=1),
+    "blocks_l16_tnd_fp8": dict(layout_q="TND", layout_k="TND", qk_dtype="e4m3fn", w_dtype="f32",
+                               N1=64, D=128, seqlens_q=[100, 7, 60], seqlens_k=[3000, 500, 60],
+                               sparse_count=64, sparse_mode=3, block_len=16, init_num=2,
+                               local_num=4),
+    "blocks_l8_paged_decode": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16",
+                                   w_dtype="bf16", N1=64, D=128, seqlens_q=[2, 2, 1],
+                                   seqlens_k=[5000, 700, 1500], sparse_count=128, sparse_mode=3,
+                                   block_size=64, block_len=8, init_num=1, local_num=2,
+                                   output_idx_offset=[0, 9, 70000]),
+    "blocks_l4_nomask_cmp": dict(layout_q="BSND", layout_k="BSND", qk_dtype="f16", w_dtype="f32",
+                                 N1=32, D=64, seqlens_q=[17], seqlens_k=[900], sparse_count=32,
+                                 sparse_mode=0, cmp_ratio=4, block_len=4, init_num=3),
+    "blocks_i8_short_rows": dict(layout_q="TND", layout_k="TND", qk_dtype="i8", w_dtype="f16",
+                                 N1=16, D=128, seqlens_q=[20, 1], seqlens_k=[20, 41],
+                                 sparse_count=12, sparse_mode=3, block_len=4, init_num=1,
+                                 local_num=1),
+    "kept_tokens": dict(layout_q="BSND", layout_k="BSND", qk_dtype="bf16", w_dtype="bf16", N1=64,
+                        D=128, seqlens_q=[200], seqlens_k=[1500], sparse_count=100,
+                        sparse_mode=3, init_num=4, local_num=4),
+    "blocks_k4096": dict(layout_q="TND", layout_k="TND", qk_dtype="bf16", w_dtype="bf16", N1=16,
+                         D=64, seqlens_q=[3, 2], seqlens_k=[9000, 40000], sparse_count=4096,
+                         sparse_mode=3, block_len=2, init_num=16, local_num=64),
 }
 
 
@@ -193,11 +219,13 @@ INT_CASES = [
     ("f16", 0, {}),
     ("bf16", 3, dict(cmp_ratio=4, cmp_residual_k=[2], output_idx_offset=[50])),
     ("f16", 0, dict(sparse_count=2500, seqlens_k=[3000])),
+    ("bf16", 3, dict(block_len=4, init_num=2, local_num=2, sparse_count=40)),
 ]
 
 
 @pytest.mark.parametrize("dt,mode,extra", INT_CASES,
-                         ids=["bf16_causal", "f16_nomask", "bf16_compressed_offset", "f16_k2500"])
+                         ids=["bf16_causal", "f16_nomask", "bf16_compressed_offset", "f16_k2500",
+                              "bf16_blocks_kept"])
 def test_integer_inputs_bit_exact(dt, mode, extra):
     wl = _integer_workload(dt, mode, **extra)
     idx, val, _, _ = I.run_workload(wl, DEV, return_value=True)
@@ -224,6 +252,26 @@ def test_zero_weights_long_rows_use_exact_fallback(sk, k):
     for i in range(2):
         assert gi[i].tolist() == list(range(k))
         assert (gv[i] == 0).all() and not np.signbit(gv[i]).any()
+
+
+@pytest.mark.parametrize("sk,L", [(3000, 1), (20000, 1), (9000, 4)])
+def test_zero_weights_with_kept_blocks(sk, L):
+    """All scores 0 with sink and local blocks: the kept blocks come first, then
+    the lowest other block indices (the exact fallback over a key range that
+    starts past the sink blocks)."""
+    k, init_num, local_num = 2048, 3, 5
+    wl = synth.build("zero_kept", layout_q="TND", layout_k="TND", qk_dtype="bf16",
+                     w_dtype="f32", N1=8, D=64, seqlens_q=[1], seqlens_k=[sk], sparse_count=k,
+                     sparse_mode=0, block_len=L, init_num=init_num, local_num=local_num, seed=12)
+    wl.w = np.zeros_like(wl.w)
+    _say(f"[gpu] zero weights with kept blocks sk={sk} L={L}")
+    idx, val, _, _ = I.run_workload(wl, DEV, return_value=True)
+    gi = idx.cpu().numpy().reshape(k)
+    nb = -(-sk // L)
+    want = [0, 1, 2] + list(range(nb - 5, nb)) + list(range(3, 3 + k - 8))
+    assert gi.tolist() == want
+    gv = val.cpu().numpy().reshape(k)
+    assert (gv == 0).all() and not np.signbit(gv).any()
 
 
 def test_zero_weights_give_lowest_indices():
