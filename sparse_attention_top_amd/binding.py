@@ -237,14 +237,14 @@ def li_indexer(p: li_problem, inputs: li_inputs, meta_host: np.ndarray, meta_dev
 
 # Layout of the task table header (mirrors MetaHeader in csrc/li_internal.h),
 # for tests and reports only.
-TOPK_CLASSES = 6
-TOPK_CLASS_KEYS = (2048, 4096, 8192, 16384, 32768, 0x7FFFFFFF)
+TOPK_CLASSES = 4
+TOPK_CLASS_KEYS = (8192, 16384, 32768, 0x7FFFFFFF)
 META_HEADER_DTYPE = np.dtype([
     ("magic", "<u4"), ("version", "<u4"), ("problem_hash", "<u8"), ("batch", "<i4"),
     ("num_items", "<i4"), ("num_rows", "<i8"), ("variant", "<i4"), ("tile_q", "<i4"),
     ("key_chunk", "<i4"), ("num_cus", "<i4"), ("ws_floats", "<i8"), ("visible_pairs", "<i8"),
     ("off_batches", "<u8"), ("off_items", "<u8"), ("max_sk", "<i4"), ("max_sq", "<i4"),
-    ("off_rows", "<u8"), ("row_class", "<i4", (TOPK_CLASSES + 2,)),
+    ("off_rows", "<u8"), ("row_class", "<i4", (TOPK_CLASSES + 4,)),
 ])
 BATCH_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("row_base", "<i4"), ("k_base", "<i4"),
                             ("s_q", "<i4"), ("s_k", "<i4"), ("ld", "<i4"), ("rows", "<i4"),

@@ -25,14 +25,14 @@ namespace li {
 // count and workspace offset so that a top-k workgroup needs one record.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMetaMagic = 0x444D494Cu;  // "LIMD"
-constexpr uint32_t kMetaVersion = 4;
+constexpr uint32_t kMetaVersion = 5;
 
 // Top-k size classes: class c holds the rows of at most kTopkClassKeys[c]
 // visible keys (the last class is unbounded) and runs with kTopkClassThreads[c]
 // threads per row.
-constexpr int kTopkClasses = 6;
-constexpr int kTopkClassKeys[kTopkClasses] = {2048, 4096, 8192, 16384, 32768, 0x7FFFFFFF};
-constexpr int kTopkClassThreads[kTopkClasses] = {256, 256, 256, 512, 1024, 1024};
+constexpr int kTopkClasses = 4;
+constexpr int kTopkClassKeys[kTopkClasses] = {8192, 16384, 32768, 0x7FFFFFFF};
+constexpr int kTopkClassThreads[kTopkClasses] = {256, 512, 1024, 1024};
 inline int topk_class(int n) {
   int c = 0;
   while (c + 1 < kTopkClasses && n > kTopkClassKeys[c]) ++c;
@@ -57,7 +57,7 @@ struct MetaHeader {
   int32_t max_sk;
   int32_t max_sq;
   uint64_t off_rows;       // byte offset of the RowRec array
-  int32_t row_class[kTopkClasses + 2];   // first RowRec of each class; [kTopkClasses] = num_rows
+  int32_t row_class[kTopkClasses + 4];   // first RowRec of each class; [kTopkClasses] = num_rows
 };
 static_assert(sizeof(MetaHeader) == 128, "header size");
 

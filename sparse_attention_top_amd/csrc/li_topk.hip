@@ -10,9 +10,11 @@
 // descending composite order. Every composite is > 0.
 //
 // One workgroup per output row. Rows are grouped by the host into size classes
-// (visible keys); each class runs a kernel whose NT threads keep the row in
-// registers (R scores per thread, loaded as float4) or, past 32K keys, re-read
-// it from memory on every pass.
+// (up to 8K, 16K, 32K visible keys, longer), each class sorted longest first so
+// that short rows fill the tail of its launch; a class runs a kernel whose NT
+// threads keep the row in registers (R scores per thread, loaded as float4) or,
+// past 32K keys, re-read it from memory on every pass. Block-wide scans and
+// min / max go through DPP lane shifts inside each wave.
 //
 // Fast path (any row whose scores spread over a finite range):
 //   1. min / max of the row (block reduction);
@@ -31,6 +33,8 @@
 // with 11/11/10-bit digits (score first, index digits only on ties at the
 // threshold), compaction of the k winners into LDS and a bitonic sort.
 #include "li_internal.h"
+
+#include <type_traits>
 
 namespace li {
 namespace {
@@ -101,18 +105,35 @@ struct Counters {
   }
 };
 
+// Inclusive prefix over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8
+// inside each 16-lane row, then row 0's / row 2's last lane broadcast into rows
+// 1 / 3 and lane 31 into rows 2 and 3. Lanes whose source lies outside the row
+// (or whose row is masked off) combine with `id`.
+template <int CTRL, int ROWS, typename T, typename Op>
+__device__ inline T dpp_step(T x, T id, Op op) {
+  const int y = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, x),
+                                            CTRL, ROWS, 0xF, false);
+  return op(x, __builtin_bit_cast(T, y));
+}
+
+template <typename T, typename Op>
+__device__ inline T wave_scan(T x, T id, Op op) {
+  x = dpp_step<0x111, 0xF>(x, id, op);   // row_shr:1
+  x = dpp_step<0x112, 0xF>(x, id, op);   // row_shr:2
+  x = dpp_step<0x114, 0xF>(x, id, op);   // row_shr:4
+  x = dpp_step<0x118, 0xF>(x, id, op);   // row_shr:8
+  x = dpp_step<0x142, 0xA>(x, id, op);   // row_bcast:15
+  x = dpp_step<0x143, 0xC>(x, id, op);   // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over the block in thread order.
 template <int NT>
 __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   uint32_t before = 0;
@@ -125,13 +146,10 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave) {
 template <int NT>
 __device__ inline void block_minmax(float& lo, float& hi, float* s_red) {
   constexpr int NW = NT / 64;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = fminf(lo, __shfl_xor(lo, o));
-    hi = fmaxf(hi, __shfl_xor(hi, o));
-  }
+  lo = wave_scan(lo, __builtin_huge_valf(), [](float a, float b) { return fminf(a, b); });
+  hi = wave_scan(hi, -__builtin_huge_valf(), [](float a, float b) { return fmaxf(a, b); });
   const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  if ((threadIdx.x & 63) == 63) {
     s_red[wave] = lo;
     s_red[NW + wave] = hi;
   }
@@ -522,11 +540,10 @@ __device__ void select_by_radix(const Row<NT, R, RES, KEPT>& row, int K, int m, 
 // One workgroup per row of one size class: row record first + blockIdx.x.
 // W16 (16-bit bucket counters) is used only for rows of at most 65535 keys.
 // A row's latency is a chain of dependent LDS and memory steps, so throughput
-// comes from rows in flight: the 256-thread kernels are held to the register
-// budget of five (8K-key rows) or six (shorter rows) workgroups per CU, six
-// being also what the LDS allows.
+// comes from rows in flight: the 256-thread kernel (every row up to 8K keys, in
+// one launch) is held to the register budget of five workgroups per CU.
 template <int NT, int R, bool RES, bool KEPT, bool W16, int KMAX>
-__global__ __launch_bounds__(NT, (NT == 256 && KMAX == kMaxKSmall) ? (R == 32 ? 5 : 6) : 1)
+__global__ __launch_bounds__(NT, (NT == 256 && KMAX == kMaxKSmall) ? 5 : 1)
 void topk_kernel(TopkArgs a, int first) {
   __shared__ Smem<NT, W16, KMAX> sm;
   const RowRec rr = a.rows[first + blockIdx.x];
@@ -594,12 +611,10 @@ hipError_t launch_class(const TopkArgs& a, int c, hipStream_t s) {
 template <int KMAX, bool KEPT>
 hipError_t launch_all(const TopkArgs& a, hipStream_t s) {
   hipError_t e;
-  if ((e = launch_class<256, 8, true, true, KMAX, KEPT>(a, 0, s)) != hipSuccess) return e;
-  if ((e = launch_class<256, 16, true, true, KMAX, KEPT>(a, 1, s)) != hipSuccess) return e;
-  if ((e = launch_class<256, 32, true, true, KMAX, KEPT>(a, 2, s)) != hipSuccess) return e;
-  if ((e = launch_class<512, 32, true, true, KMAX, KEPT>(a, 3, s)) != hipSuccess) return e;
-  if ((e = launch_class<1024, 32, true, true, KMAX, KEPT>(a, 4, s)) != hipSuccess) return e;
-  return launch_class<1024, 4, false, false, KMAX, KEPT>(a, 5, s);
+  if ((e = launch_class<256, 32, true, true, KMAX, KEPT>(a, 0, s)) != hipSuccess) return e;
+  if ((e = launch_class<512, 32, true, true, KMAX, KEPT>(a, 1, s)) != hipSuccess) return e;
+  if ((e = launch_class<1024, 32, true, true, KMAX, KEPT>(a, 2, s)) != hipSuccess) return e;
+  return launch_class<1024, 4, false, false, KMAX, KEPT>(a, 3, s);
 }
 
 template <bool KEPT>
@@ -613,12 +628,11 @@ hipError_t launch_topk(const li_problem& p, const TopkArgs& a, hipStream_t s) {
   (void)p;
   if (a.k < 1 || a.k > kMaxKLarge) return hipErrorInvalidValue;
   // Resident capacities NT*R must equal the class limits kTopkClassKeys.
-  static_assert(256 * 8 == kTopkClassKeys[0] && 256 * 16 == kTopkClassKeys[1] &&
-                    256 * 32 == kTopkClassKeys[2] && 512 * 32 == kTopkClassKeys[3] &&
-                    1024 * 32 == kTopkClassKeys[4],
+  static_assert(256 * 32 == kTopkClassKeys[0] && 512 * 32 == kTopkClassKeys[1] &&
+                    1024 * 32 == kTopkClassKeys[2],
                 "class capacities");
-  static_assert(kTopkClassThreads[0] == 256 && kTopkClassThreads[3] == 512 &&
-                    kTopkClassThreads[4] == 1024 && kTopkClassThreads[5] == 1024,
+  static_assert(kTopkClassThreads[0] == 256 && kTopkClassThreads[1] == 512 &&
+                    kTopkClassThreads[2] == 1024 && kTopkClassThreads[3] == 1024,
                 "class thread counts");
   return (a.init_num > 0 || a.local_num > 0) ? launch_k<true>(a, s) : launch_k<false>(a, s);
 }
