@@ -407,16 +407,21 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
     }
     return p0 + p1;
   };
+  // The last slice's epilogue, with the same accumulation order as the one
+  // interleaved in step(), so a key's score does not depend on which slice of
+  // its item it falls in.
   auto epi = [&](const Acc (&acc)[NT]) {
     float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        p0 = fmaf(wr[t][e], M::relu(acc[t], e), p0);
-        p1 = fmaf(wr[t][e + 1], M::relu(acc[t], e + 1), p1);
-      }
-    }
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int u = 0; u < EPM; u += 2) {
+          const int e = s * EPM + u;
+          p0 = fmaf(wr[t][e], M::relu(acc[t], e), p0);
+          p1 = fmaf(wr[t][e + 1], M::relu(acc[t], e + 1), p1);
+        }
     return p0 + p1;
   };
   // Cross-half swap-add (both halves end up with the full sum over heads) and

@@ -297,6 +297,23 @@ def test_deterministic_bitwise():
     assert torch.equal(i1, i2) and torch.equal(v1, v2)
 
 
+@pytest.mark.parametrize("name", ["paged_decode_cut", "prefill_cut"])
+def test_work_decomposition_does_not_change_results(name):
+    """The task table splits rows into different key chunks for different CU
+    counts; every key's score is computed in the same order wherever its chunk
+    ends, so indices and values are bit-identical."""
+    wl = (synth.paged_decode(B=6, lo=3000, hi=20000, sparse_count=512) if name == "paged_decode_cut"
+          else synth.dsa_prefill(S=1500, sparse_count=256))
+    outs = []
+    for cus in (256, 37, 8):
+        idx, val, plan, _ = I.run_workload(wl, DEV, return_value=True, num_cus=cus)
+        _say(f"[gpu] {name}: num_cus={cus} items={int(plan.header['num_items'])} "
+             f"chunk={int(plan.header['key_chunk'])}")
+        outs.append((idx, val))
+    for idx, val in outs[1:]:
+        assert torch.equal(idx, outs[0][0]) and torch.equal(val, outs[0][1])
+
+
 def test_values_flag_does_not_change_indices():
     wl = synth.test_shape(S1=64, S2=900, sparse_count=200)
     i1, _, _, _ = I.run_workload(wl, DEV, return_value=False)
