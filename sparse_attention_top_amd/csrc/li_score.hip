@@ -401,6 +401,9 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
           p0 = fmaf(wr[t][e], M::relu(old[t], e), p0);
           p1 = fmaf(wr[t][e + 1], M::relu(old[t], e + 1), p1);
         }
+        // Keep this share of the epilogue between its MFMAs: without the pin
+        // the IR passes sink the whole ReLU / weight chain behind the last MFMA.
+        asm volatile("" : "+v"(p0), "+v"(p1));
         __builtin_amdgcn_sched_barrier(0);
       }
       bf[s] = read_frag(nbase, s);
