@@ -92,8 +92,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the indexer on one GPU only; multi-GPU runs are not part "
-              "of this build (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures the indexer on one GPU only: rows shard across GPUs with "
+              "no exchange, so the multi-GPU figure is N times the one-GPU rate and is not "
+              "run here.", file=sys.stderr)
         sys.exit(2)
 
     import torch
