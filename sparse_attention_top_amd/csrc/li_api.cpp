@@ -196,8 +196,10 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
                "TND queries need cu_seqlens_q");
       LI_CHECK(L->cu_seqlens_q[0] == 0, LI_ERR_INVALID_ARGUMENT, "cu_seqlens_q[0] must be 0");
       for (int b = 0; b < B; ++b) {
-        const int32_t n = L->cu_seqlens_q[b + 1] - L->cu_seqlens_q[b];
-        LI_CHECK(n >= 0, LI_ERR_INVALID_ARGUMENT, "cu_seqlens_q must be non-decreasing");
+        const int64_t n64 = (int64_t)L->cu_seqlens_q[b + 1] - L->cu_seqlens_q[b];
+        LI_CHECK(n64 >= 0 && L->cu_seqlens_q[b] >= 0, LI_ERR_INVALID_ARGUMENT,
+                 "cu_seqlens_q must be non-decreasing from 0");
+        const int32_t n = (int32_t)n64;
         rows[b] = n;
         row_base[b] = L->cu_seqlens_q[b];
         sq[b] = n;
@@ -212,6 +214,8 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     } else {
       LI_CHECK(L->cu_seqlens_q == nullptr, LI_ERR_INVALID_ARGUMENT,
                "BSND queries do not take cu_seqlens_q");
+      LI_CHECK((int64_t)B * p->s1 < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED,
+               "batch * s1 must be below 2^31");
       for (int b = 0; b < B; ++b) {
         rows[b] = p->s1;
         row_base[b] = b * p->s1;
@@ -222,15 +226,15 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
           sq[b] = L->seqused_q[b];
         }
       }
-      LI_CHECK((int64_t)B * p->s1 < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED,
-               "batch * s1 must be below 2^31");
     }
     if (p->layout_k == LI_LAYOUT_TND) {
       LI_CHECK(L->cu_seqlens_k != nullptr, LI_ERR_INVALID_ARGUMENT, "TND keys need cu_seqlens_k");
       LI_CHECK(L->cu_seqlens_k[0] == 0, LI_ERR_INVALID_ARGUMENT, "cu_seqlens_k[0] must be 0");
       for (int b = 0; b < B; ++b) {
-        const int32_t n = L->cu_seqlens_k[b + 1] - L->cu_seqlens_k[b];
-        LI_CHECK(n >= 0, LI_ERR_INVALID_ARGUMENT, "cu_seqlens_k must be non-decreasing");
+        const int64_t n64 = (int64_t)L->cu_seqlens_k[b + 1] - L->cu_seqlens_k[b];
+        LI_CHECK(n64 >= 0 && L->cu_seqlens_k[b] >= 0, LI_ERR_INVALID_ARGUMENT,
+                 "cu_seqlens_k must be non-decreasing from 0");
+        const int32_t n = (int32_t)n64;
         k_base[b] = L->cu_seqlens_k[b];
         sk[b] = n;
         if (L->seqused_k) {
@@ -244,6 +248,8 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     } else if (p->layout_k == LI_LAYOUT_BSND) {
       LI_CHECK(L->cu_seqlens_k == nullptr, LI_ERR_INVALID_ARGUMENT,
                "BSND keys do not take cu_seqlens_k");
+      LI_CHECK((int64_t)B * p->s2 < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED,
+               "batch * s2 must be below 2^31");
       for (int b = 0; b < B; ++b) {
         k_base[b] = b * p->s2;
         sk[b] = p->s2;
@@ -253,8 +259,6 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
           sk[b] = L->seqused_k[b];
         }
       }
-      LI_CHECK((int64_t)B * p->s2 < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED,
-               "batch * s2 must be below 2^31");
     } else {
       LI_CHECK(L->cu_seqlens_k == nullptr, LI_ERR_INVALID_ARGUMENT,
                "PA_BSND keys do not take cu_seqlens_k");

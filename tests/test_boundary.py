@@ -119,6 +119,8 @@ LEN_BAD = [
      dict(cu_seqlens_q=[1, 8], cu_seqlens_k=[0, 8])),
     ("cu_seqlens decreasing", dict(layout_q="TND", layout_k="TND", t1=8, t2=8, batch=2),
      dict(cu_seqlens_q=[0, 9, 8], cu_seqlens_k=[0, 4, 8])),
+    ("cu_seqlens negative entry", dict(layout_q="TND", layout_k="TND", t1=8, t2=8, batch=2),
+     dict(cu_seqlens_q=[0, -2**31, 8], cu_seqlens_k=[0, 4, 8])),
     ("cu_seqlens total", dict(layout_q="TND", layout_k="TND", t1=8, t2=8, batch=1),
      dict(cu_seqlens_q=[0, 7], cu_seqlens_k=[0, 8])),
     ("seqused_q above s1", dict(), dict(seqused_q=[17, 3])),
