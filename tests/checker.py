@@ -1,14 +1,18 @@
 """GPU-vs-oracle acceptance rule for one indexer output row.
 
 Let s be the oracle's float64 scores of the row's visible keys (n of them),
-m = min(k, n), s_(k) the k-th largest score, s_(1) the largest, and
-tau = tol * max(|s_(k)|, 2^-6 * |s_(1)|) (tol = 1e-3 for fp16/bf16 inputs,
-2e-2 for fp8/int8). The GPU row G is accepted iff
+m = min(k, n), s_(k) the k-th largest score, M = max_j |s_j| the row's
+largest score magnitude, and tau = tol * max(|s_(k)|, 2^-6 * M) (tol = 1e-3
+for fp16/bf16 inputs, 2e-2 for fp8/int8). The floor 2^-6 * M keeps the band
+from vanishing near zero: the GPU sums the head dot products in float32, so
+its error scales with the row's magnitudes, not with a score that cancels to
+about zero (a row whose weights are all negative has every score <= 0, its
+largest score is 0, and only M gives the scale). The GPU row G is accepted iff
   1. its first m entries are distinct visible keys and the rest are -1;
   2. every j in G has s_j >= s_(k) - tau;
   3. every visible j with s_j > s_(k) + tau is in G;
   4. consecutive entries are ordered by score within tau;
-  5. returned values v_j satisfy |v_j - s_j| <= tol * max(|s_j|, 2^-6 |s_(1)|),
+  5. returned values v_j satisfy |v_j - s_j| <= tol * max(|s_j|, 2^-6 M),
      are non-increasing, and the tail holds -inf.
 Rules 2-3 make G equal the oracle's set whenever s_(k) and s_(k+1) are more
 than tau apart; inside that band any choice whose oracle score is within tau
@@ -71,7 +75,7 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
             assert np.isneginf(gval).all(), f"{where}: values of an empty row must be -inf"
         return
     srt = np.sort(s)[::-1]
-    s1 = abs(srt[0])
+    s1 = np.abs(s).max()
     floor = 2.0 ** -6 * s1
     if n <= k:
         assert np.array_equal(np.sort(head), np.arange(n)), f"{where}: must return every key"

@@ -196,6 +196,61 @@ def test_edge_cases_all_rows(name):
     run_and_check(wl, label=name)
 
 
+def _random_case(seed):
+    """A seeded random problem inside the documented limits: layout, dtypes, head
+    count, head dim, lengths (empty and ragged included), mode, k, compressed
+    keys, index offsets and key blocks all drawn; sizes stay small enough for
+    the oracle to check every row."""
+    rng = np.random.default_rng(7000 + seed)
+    pick = lambda xs: xs[int(rng.integers(len(xs)))]
+    layout = pick(["BSND", "TND", "PA"])
+    qk = pick(["f16", "bf16", "e4m3fn", "i8"])
+    w = pick(["f16", "bf16", "f32"])
+    B = int(rng.integers(1, 5))
+    sk = [int(x) for x in rng.integers(0, 1500, B)]
+    sq = [int(rng.integers(0, min(s, 120) + 2)) if s else int(rng.integers(0, 3)) for s in sk]
+    if rng.random() < 0.3:   # decode-shaped
+        sq = [int(rng.integers(0, 3)) for _ in range(B)]
+    if sum(sq) == 0:
+        sq[0] = 1
+    if sum(sk) == 0:
+        sk[0] = 17
+    mode = pick([0, 3])
+    k = pick([1, 7, 64, 200, 513, 2048, 3000])
+    kw = dict(layout_q="TND" if layout == "TND" else "BSND",
+              layout_k={"BSND": "BSND", "TND": "TND", "PA": "PA_BSND"}[layout],
+              qk_dtype=qk, w_dtype=w, N1=pick([1, 8, 32, 48, 64]), D=pick([64, 128]),
+              seqlens_q=sq, seqlens_k=sk, sparse_count=k, sparse_mode=mode)
+    if layout == "PA":
+        kw["block_size"] = pick([16, 48, 64, 128, 256])
+    if layout == "BSND":
+        kw["S1"], kw["S2"] = max(sq) + int(rng.integers(0, 3)), max(sk) + int(rng.integers(0, 5))
+    if rng.random() < 0.3:
+        r = pick([2, 4, 16, 128])
+        kw["cmp_ratio"] = r
+        if mode == 3:
+            kw["cmp_residual_k"] = [int(x) for x in rng.integers(0, r, B)]
+    if rng.random() < 0.3:
+        kw["output_idx_offset"] = [int(x) for x in rng.integers(0, 100000, B)]
+    if rng.random() < 0.3:
+        kw["block_len"] = pick([2, 4, 8, 16])
+    if rng.random() < 0.3:
+        kw["init_num"] = int(rng.integers(0, 4))
+        kw["local_num"] = int(rng.integers(0, 4))
+        kw["sparse_count"] = max(k, kw["init_num"] + kw["local_num"])
+    return synth.build(f"random{seed}", seed=seed, **kw)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_problems_all_rows(seed):
+    wl = _random_case(seed)
+    _say(f"[gpu] random{seed}: {wl.layout_q}/{wl.layout_k} {wl.qk_dtype}/{wl.w_dtype} "
+         f"N1={wl.N1} D={wl.D} sq={list(wl.seqlens_q)} sk={list(wl.seqlens_k)} "
+         f"k={wl.sparse_count} mode={wl.sparse_mode} cmp={wl.cmp_ratio} L={wl.block_len} "
+         f"kept={wl.init_num}+{wl.local_num}")
+    run_and_check(wl, label=f"random{seed}")
+
+
 def _integer_workload(qk_dtype="bf16", mode=3, seed=5, **extra):
     """Small-integer q/k and power-of-two weights: every score is exact in fp32,
     so GPU and oracle must agree bit for bit, ties (lowest index first) included."""
