@@ -241,7 +241,37 @@ def _random_case(seed):
     return synth.build(f"random{seed}", seed=seed, **kw)
 
 
-@pytest.mark.parametrize("seed", range(24))
+def _random_long_case(seed):
+    """Few query rows over long key ranges (every top-k size class, streamed rows
+    included), k up to 8192, TND or paged keys."""
+    rng = np.random.default_rng(9000 + seed)
+    pick = lambda xs: xs[int(rng.integers(len(xs)))]
+    B = int(rng.integers(1, 4))
+    sk = [int(x) for x in rng.integers(1, 45000, B)]
+    sq = [int(rng.integers(1, 3)) for _ in range(B)]
+    paged = bool(rng.integers(2))
+    kw = dict(layout_q="BSND" if paged else "TND", layout_k="PA_BSND" if paged else "TND",
+              qk_dtype=pick(["bf16", "f16", "e4m3fn"]), w_dtype=pick(["bf16", "f32"]),
+              N1=pick([8, 64]), D=pick([64, 128]), seqlens_q=sq, seqlens_k=sk,
+              sparse_count=pick([100, 2048, 4096, 8192]), sparse_mode=pick([0, 3]))
+    if paged:
+        kw["block_size"] = pick([64, 128, 1024])
+    if rng.random() < 0.3:
+        kw["block_len"] = pick([2, 8])
+        kw["init_num"], kw["local_num"] = 1, 4
+    return synth.build(f"random_long{seed}", seed=seed, **kw)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_long_rows_all_rows(seed):
+    wl = _random_long_case(seed)
+    _say(f"[gpu] random_long{seed}: {wl.layout_q}/{wl.layout_k} {wl.qk_dtype} N1={wl.N1} "
+         f"D={wl.D} sq={list(wl.seqlens_q)} sk={list(wl.seqlens_k)} k={wl.sparse_count} "
+         f"mode={wl.sparse_mode} L={wl.block_len}")
+    run_and_check(wl, label=f"random_long{seed}")
+
+
+@pytest.mark.parametrize("seed", range(48))
 def test_random_problems_all_rows(seed):
     wl = _random_case(seed)
     _say(f"[gpu] random{seed}: {wl.layout_q}/{wl.layout_k} {wl.qk_dtype}/{wl.w_dtype} "
