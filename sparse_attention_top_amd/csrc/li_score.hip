@@ -224,7 +224,10 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
   // Key staging. Stage st covers keys [k0 + st*KT, k0 + (st+1)*KT); keys past
   // k1 are clamped to the item's last key (computed, never stored), so every
   // load is unconditional. For the paged cache the block ids of a stage are
-  // loaded one stage before its keys.
+  // loaded one stage before its keys, with scalar loads: a 1 KB DMA block holds
+  // 1024/ROW <= 16 consecutive keys starting at a multiple of 1024/ROW, and cache
+  // blocks are multiples of 16 keys, so all its keys (clamped ones included)
+  // share one cache block, the one of its first key.
   const bool paged = a.layout_k == LI_LAYOUT_PA_BSND;
   const int jmax = it.k1 - 1;
   const int32_t* btab = a.block_table + (int64_t)it.b * a.max_blocks;
@@ -244,10 +247,12 @@ __global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
   };
   int pid[DPW];
   int psid = 0;
+  const auto* btab_s = (const __attribute__((address_space(4))) int32_t*)btab;
   auto ids = [&](int st) {
     if (!paged) return;
 #pragma unroll
-    for (int d = 0; d < DPW; ++d) pid[d] = btab[block_index(stage_key(st, dma_row(d)))];
+    for (int d = 0; d < DPW; ++d)
+      pid[d] = btab_s[block_index(stage_key(st, (d * NW + wave) * 1024 / ROW))];
     if (QUANT) psid = btab[block_index(stage_key(st, tid % KT))];
   };
   float pre_sc = 0.f;
