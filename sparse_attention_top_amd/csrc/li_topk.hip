@@ -32,6 +32,12 @@
 // kSegMax keys, e.g. many equal scores): MSD radix select over the composite
 // with 11/11/10-bit digits (score first, index digits only on ties at the
 // threshold), compaction of the k winners into LDS and a bitonic sort.
+//
+// Routing options of the ops-transformer issue's forward operator: the blocks
+// that are always kept (the first init_num and the last local_num of a row) are
+// written first, in ascending order, and the selection above runs over the
+// blocks between them for the remaining slots (the KEPT kernels). Every stored
+// index gets the batch's output_idx_offset.
 #include "li_internal.h"
 
 #include <type_traits>
