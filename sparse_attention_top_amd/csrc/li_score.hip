@@ -12,15 +12,18 @@
 // Work decomposition (one workgroup per work item of the task table):
 //   * the workgroup owns WQ query rows of one sequence and a key range [k0,k1);
 //   * 8 waves (two per SIMD, so one can issue while the other waits) = WQ rows x
-//     WK key slices; a wave holds its row's query heads in AGPRs as MFMA
+//     WK key slices; a wave holds its row's query heads in VGPRs as MFMA
 //     A-operands for the whole key loop;
-//   * keys are staged KT at a time in LDS (double buffered through registers),
-//     gathered through the block table for the paged layout;
+//   * keys are staged KT at a time in two LDS buffers by direct global -> LDS
+//     loads (no staging registers), gathered through the block table for the
+//     paged layout;
 //   * per 32-key slice a wave runs NT x (D / k-step) MFMA 32x32 ops with heads on
 //     the M axis and keys on the N axis, with B fragments read one slice ahead;
 //     each lane then holds 16 heads of one key per tile, applies ReLU and the
 //     per-head weight (interleaved with the next slice's MFMAs), and one
-//     cross-lane swap-add over the two half-waves completes the reduction.
+//     cross-lane swap-add over the two half-waves completes the reduction;
+//   * with key blocks (block_len > 1) the maximum over each block's visible keys
+//     is taken across lanes before the store, so one float per block leaves.
 #include "li_internal.h"
 
 #include <utility>
