@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define LI_API_VERSION 3
+#define LI_API_VERSION 4
 
 typedef enum li_status {
   LI_OK = 0,
@@ -235,7 +235,9 @@ li_status li_metadata(const li_problem* p, const li_lengths* lengths, int32_t nu
 
 /*
  * li_workspace_size -- host-only: bytes of device workspace li_score/li_indexer
- * need (the head-reduced float32 scores of every visible (row, key) pair).
+ * need: the head-reduced float32 scores of every visible (row, key) pair and,
+ * when the task table splits long rows (few rows, k <= 2048), the candidate
+ * lists that li_topk passes between its two passes.
  */
 li_status li_workspace_size(const li_problem* p, const void* meta_host, size_t* bytes);
 
@@ -251,11 +253,13 @@ li_status li_score(const li_problem* p, const li_inputs* in, const void* meta_ho
 
 /*
  * li_topk -- enqueue the per-row top-k over a workspace filled by li_score.
+ *  ws, ws_bytes    the workspace li_score filled; the scores are only read, the
+ *                  candidate-list part (split rows) is written.
  *  sparse_indices  device int32, (B,S1,N2,k) or (T1,N2,k).
  *  sparse_values   device float32 of the same shape; required iff return_value.
  */
 li_status li_topk(const li_problem* p, const void* meta_host, const void* meta_dev,
-                  const void* ws, size_t ws_bytes, int32_t* sparse_indices,
+                  void* ws, size_t ws_bytes, int32_t* sparse_indices,
                   float* sparse_values, void* stream);
 
 /* li_indexer -- li_score followed by li_topk on the same stream. */

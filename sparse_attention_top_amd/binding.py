@@ -16,7 +16,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libli_mi355x.so")
 
-API_VERSION = 3
+API_VERSION = 4
 INT64_MAX = (1 << 63) - 1
 
 # li_status
@@ -244,14 +244,18 @@ META_HEADER_DTYPE = np.dtype([
     ("num_items", "<i4"), ("num_rows", "<i8"), ("variant", "<i4"), ("tile_q", "<i4"),
     ("key_chunk", "<i4"), ("num_cus", "<i4"), ("ws_floats", "<i8"), ("visible_pairs", "<i8"),
     ("off_batches", "<u8"), ("off_items", "<u8"), ("max_sk", "<i4"), ("max_sq", "<i4"),
-    ("off_rows", "<u8"), ("row_class", "<i4", (TOPK_CLASSES + 4,)),
+    ("off_rows", "<u8"), ("row_class", "<i4", (2 * TOPK_CLASSES + 1,)), ("split_rows", "<i4"),
+    ("cand_val_off", "<i8"), ("cand_idx_off", "<i8"), ("num_recs", "<i8"),
+    ("reserved", "<i4", (4,)),
 ])
+assert META_HEADER_DTYPE.itemsize == 176
 BATCH_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("row_base", "<i4"), ("k_base", "<i4"),
                             ("s_q", "<i4"), ("s_k", "<i4"), ("ld", "<i4"), ("rows", "<i4"),
                             ("cmp_res", "<i4"), ("reserved", "<i4")])
 WORK_ITEM_DTYPE = np.dtype([("b", "<i4"), ("q0", "<i4"), ("k0", "<i4"), ("k1", "<i4")])
-ROW_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("row", "<i4"), ("n", "<i4"),
-                          ("idx_offset", "<i4"), ("reserved", "<i4")])
+ROW_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("out_off", "<i8"), ("n", "<i4"),
+                          ("idx_offset", "<i4"), ("row", "<i4"), ("kind", "<i4")])
+ROW_WHOLE, ROW_CHUNK, ROW_MERGE = 0, 1, 2   # top-k record kinds
 
 
 def parse_metadata(meta: np.ndarray):
@@ -264,8 +268,9 @@ def parse_metadata(meta: np.ndarray):
 
 
 def parse_row_table(meta: np.ndarray):
-    """The top-k row records and the class boundaries (TOPK_CLASSES + 1 entries)."""
+    """The top-k records of both passes and their boundaries: pass q, class c is
+    records [bounds[q*TOPK_CLASSES + c], bounds[q*TOPK_CLASSES + c + 1])."""
     h = parse_metadata(meta)[0]
     orow = int(h["off_rows"])
-    rows = meta[orow:orow + ROW_REC_DTYPE.itemsize * int(h["num_rows"])].view(ROW_REC_DTYPE)
-    return rows, np.array(h["row_class"][:TOPK_CLASSES + 1])
+    rows = meta[orow:orow + ROW_REC_DTYPE.itemsize * int(h["num_recs"])].view(ROW_REC_DTYPE)
+    return rows, np.array(h["row_class"])

@@ -378,27 +378,65 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
                      [](const Cand& x, const Cand& y) { return x.cost > y.cost; });
     LI_CHECK(cands.size() < ((size_t)1 << 31), LI_ERR_UNSUPPORTED, "too many work items");
 
-    // ---- top-k row table: rows grouped by size class, longest first ----
+    // ---- top-k records: two passes, each grouped by size class, longest first ----
     const int64_t nrows = num_rows(*p);
     LI_CHECK(nrows < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED, "too many output rows");
-    std::vector<std::vector<RowRec>> by_class(kTopkClasses);
+    const int32_t K = p->sparse_count;
+    // Split long rows only where rows are too few to fill the CUs (a split adds
+    // a pass over k candidates per chunk) and never with always-kept blocks.
+    const bool may_split = K <= kSplitMaxK && p->init_num == 0 && p->local_num == 0 &&
+                           nrows < (int64_t)kSplitRowsPerCu * num_cus;
+    // Candidate lists live after the scores: values, then indices.
+    const int64_t cand_val_off = (ws + 3) / 4 * 4;
+    int64_t cand = 0;   // candidate floats allotted so far (multiple of 4 per split row)
+    std::vector<std::vector<RowRec>> pass[2];
+    pass[0].resize(kTopkClasses);
+    pass[1].resize(kTopkClasses);
     int64_t covered = 0;
+    int32_t split_rows = 0;
     for (int b = 0; b < B; ++b) {
       for (int i = 0; i < rows[b]; ++i) {
         const int n = i < sq[b] ? blocks(visible(b, i)) : 0;
         const int64_t off = n > 0 ? recs[b].ws_off + (int64_t)i * recs[b].ld : 0;
-        by_class[topk_class(n)].push_back({off, (int32_t)(row_base[b] + i), n, ioff[b], 0});
+        const int32_t row = (int32_t)(row_base[b] + i);
+        if (!may_split || n <= kTopkClassKeys[0]) {
+          pass[0][topk_class(n)].push_back({off, (int64_t)row * K, n, ioff[b], row, kRowWhole});
+          continue;
+        }
+        // Chunk q covers keys [e_q, e_{q+1}) with e_q = 4*floor(q*n / (4c)):
+        // 16-byte aligned starts, lengths within 4 of n/c, so in
+        // (kSplitKeys/2 - 4, kSplitKeys + 4] -- above k and inside class 0.
+        const int64_t c = ((int64_t)n + kSplitKeys - 1) / kSplitKeys;
+        auto edge = [&](int64_t q) { return q >= c ? (int64_t)n : 4 * ((q * n) / (4 * c)); };
+        for (int64_t q = 0; q < c; ++q) {
+          const int64_t e0 = edge(q), e1 = edge(q + 1);
+          pass[0][0].push_back({off + e0, cand + q * K, (int32_t)(e1 - e0), (int32_t)e0, row,
+                                kRowChunk});
+        }
+        const int64_t nc = c * K;
+        LI_CHECK(nc < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED, "row %d has too many candidates",
+                 row);
+        pass[1][topk_class((int)nc)].push_back(
+            {cand_val_off + cand, (int64_t)row * K, (int32_t)nc, ioff[b], row, kRowMerge});
+        cand += (nc + 3) / 4 * 4;
+        ++split_rows;
       }
       covered += rows[b];
     }
     LI_CHECK(covered == nrows, LI_ERR_INVALID_ARGUMENT,
              "sequences cover %lld output rows, the problem has %lld", (long long)covered,
              (long long)nrows);
+    const int64_t cand_idx_off = cand_val_off + cand;
+    if (cand > 0) ws = cand_idx_off + cand;
+    int64_t nrecs = 0;
+    for (int q = 0; q < 2; ++q)
+      for (const auto& v : pass[q]) nrecs += (int64_t)v.size();
+    LI_CHECK(nrecs < ((int64_t)1 << 31), LI_ERR_UNSUPPORTED, "too many top-k records");
 
     const size_t off_b = sizeof(MetaHeader);
     const size_t off_i = off_b + sizeof(BatchRec) * (size_t)B;
     const size_t off_r = off_i + sizeof(WorkItem) * cands.size();
-    const size_t need = off_r + sizeof(RowRec) * (size_t)nrows;
+    const size_t need = off_r + sizeof(RowRec) * (size_t)nrecs;
     *meta_bytes = need;
     if (meta_host == nullptr) return LI_OK;
     LI_CHECK(meta_capacity >= need, LI_ERR_BUFFER_TOO_SMALL,
@@ -423,20 +461,26 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     h.max_sk = max_sk;
     h.max_sq = max_sq;
     h.off_rows = off_r;
+    h.split_rows = split_rows;
+    h.cand_val_off = cand > 0 ? cand_val_off : 0;
+    h.cand_idx_off = cand > 0 ? cand_idx_off : 0;
+    h.num_recs = nrecs;
     uint8_t* dst = static_cast<uint8_t*>(meta_host);
     std::memcpy(dst + off_b, recs.data(), sizeof(BatchRec) * (size_t)B);
     WorkItem* items = reinterpret_cast<WorkItem*>(dst + off_i);
     for (size_t n = 0; n < cands.size(); ++n) items[n] = cands[n].w;
     RowRec* rrecs = reinterpret_cast<RowRec*>(dst + off_r);
     int32_t pos = 0;
-    for (int c = 0; c < kTopkClasses; ++c) {
-      auto& v = by_class[c];
-      std::stable_sort(v.begin(), v.end(),
-                       [](const RowRec& x, const RowRec& y) { return x.n > y.n; });
-      h.row_class[c] = pos;
-      for (const RowRec& rc : v) rrecs[pos++] = rc;
+    for (int q = 0; q < 2; ++q) {
+      for (int c = 0; c < kTopkClasses; ++c) {
+        auto& v = pass[q][c];
+        std::stable_sort(v.begin(), v.end(),
+                         [](const RowRec& x, const RowRec& y) { return x.n > y.n; });
+        h.row_class[q * kTopkClasses + c] = pos;
+        for (const RowRec& rc : v) rrecs[pos++] = rc;
+      }
     }
-    h.row_class[kTopkClasses] = pos;
+    h.row_class[2 * kTopkClasses] = pos;
     std::memcpy(dst, &h, sizeof h);
     return LI_OK;
   } catch (const std::exception& e) {
@@ -512,7 +556,7 @@ li_status li_score(const li_problem* p, const li_inputs* in, const void* meta_ho
 }
 
 li_status li_topk(const li_problem* p, const void* meta_host, const void* meta_dev,
-                  const void* ws, size_t ws_bytes, int32_t* sparse_indices,
+                  void* ws, size_t ws_bytes, int32_t* sparse_indices,
                   float* sparse_values, void* stream) {
   li_status st = check_problem(p);
   if (st != LI_OK) return st;
@@ -536,7 +580,11 @@ li_status li_topk(const li_problem* p, const void* meta_host, const void* meta_d
   a.k = p->sparse_count;
   a.init_num = p->init_num;
   a.local_num = p->local_num;
-  for (int c = 0; c <= kTopkClasses; ++c) a.row_class[c] = h->row_class[c];
+  a.cand_val_off = h->cand_val_off;
+  a.cand_val = h->split_rows > 0 ? static_cast<float*>(ws) + h->cand_val_off : nullptr;
+  a.cand_idx = h->split_rows > 0 ? reinterpret_cast<int32_t*>(static_cast<float*>(ws) + h->cand_idx_off)
+                                 : nullptr;
+  for (int c = 0; c <= 2 * kTopkClasses; ++c) a.row_class[c] = h->row_class[c];
   const hipError_t e = launch_topk(*p, a, (hipStream_t)stream);
   LI_CHECK(e == hipSuccess, LI_ERR_HIP, "top-k kernel launch: %s", hipGetErrorString(e));
   return LI_OK;

@@ -13,19 +13,23 @@ namespace li {
 // ---------------------------------------------------------------------------
 // Task table written by li_metadata (host), read by the kernels (device).
 //
-//   [MetaHeader][BatchRec x batch][WorkItem x num_items]
-//
-//   [MetaHeader][BatchRec x batch][WorkItem x num_items][RowRec x num_rows]
+//   [MetaHeader][BatchRec x batch][WorkItem x num_items][RowRec x num_recs]
 //
 // Each BatchRec describes one sequence; each WorkItem is one workgroup of the
 // score kernel: query rows [q0, q0 + tile_q) of sequence b against keys
 // [k0, k1). Items are sorted by descending visible-pair count. Each RowRec is
-// one output row for the top-k kernels, grouped by size class (visible keys)
-// and, inside a class, longest row first; it carries the row's visible-key
-// count and workspace offset so that a top-k workgroup needs one record.
+// one top-k workgroup: it carries the visible-key count, the workspace offset
+// of the scores and where the result goes, so that the workgroup needs one
+// record. Records run in two passes, each grouped by size class and, inside a
+// class, longest first. Normally every output row is one record of the first
+// pass. When a problem has few rows (fewer than two per CU) and k <= 2048, a
+// row of more than kSplitKeys keys is split instead: each of its chunks (at
+// most kSplitKeys keys, more than k) is a first-pass record that writes its
+// sorted top k (indices and values) to a candidate list in the workspace, and
+// a second-pass record selects the row's top k among the chunk lists.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMetaMagic = 0x444D494Cu;  // "LIMD"
-constexpr uint32_t kMetaVersion = 5;
+constexpr uint32_t kMetaVersion = 6;
 
 // Top-k size classes: class c holds the rows of at most kTopkClassKeys[c]
 // visible keys (the last class is unbounded) and runs with kTopkClassThreads[c]
@@ -38,6 +42,13 @@ inline int topk_class(int n) {
   while (c + 1 < kTopkClasses && n > kTopkClassKeys[c]) ++c;
   return c;
 }
+
+// Row splitting: chunk length bound (a multiple-of-4 split of a row into
+// ceil(n / kSplitKeys) chunks keeps every chunk within the first class), the
+// largest k it is used for, and the row count below which (per CU) it is used.
+constexpr int kSplitKeys = 8188;
+constexpr int kSplitMaxK = 2048;
+constexpr int kSplitRowsPerCu = 2;
 
 struct MetaHeader {
   uint32_t magic;
@@ -57,9 +68,16 @@ struct MetaHeader {
   int32_t max_sk;
   int32_t max_sq;
   uint64_t off_rows;       // byte offset of the RowRec array
-  int32_t row_class[kTopkClasses + 4];   // first RowRec of each class; [kTopkClasses] = num_rows
+  // First RowRec of each class of each pass: pass q, class c starts at
+  // row_class[q * kTopkClasses + c]; row_class[2 * kTopkClasses] = num_recs.
+  int32_t row_class[2 * kTopkClasses + 1];
+  int32_t split_rows;      // output rows handled by chunks + a second-pass record
+  int64_t cand_val_off;    // workspace float offset of the candidate values
+  int64_t cand_idx_off;    // ... of the candidate indices (int32 in float slots)
+  int64_t num_recs;        // RowRec records of both passes
+  int32_t reserved[4];
 };
-static_assert(sizeof(MetaHeader) == 128, "header size");
+static_assert(sizeof(MetaHeader) == 176, "header size");
 
 struct BatchRec {
   int64_t ws_off;   // first workspace float of the sequence
@@ -79,15 +97,26 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == 16, "work item size");
 
-struct RowRec {
-  int64_t ws_off;      // first workspace float of the row's scores
-  int32_t row;         // output row (B*S1 rows for BSND, T1 for TND)
-  int32_t n;           // visible keys, or visible key blocks when block_len > 1
-                       // (0 for rows past a sequence's actual length)
-  int32_t idx_offset;  // added to every returned index (output_idx_offset)
-  int32_t reserved;
+// What a top-k record selects from and where its result goes.
+enum RowKind : int32_t {
+  kRowWhole = 0,  // an output row: scores -> output row
+  kRowChunk = 1,  // a chunk of a split row: scores -> candidate list (indices and values)
+  kRowMerge = 2,  // a split row: its chunks' candidate lists -> output row
 };
-static_assert(sizeof(RowRec) == 24, "row record size");
+
+struct RowRec {
+  int64_t ws_off;      // first workspace float of the scores (kRowMerge: candidate values)
+  int64_t out_off;     // first output element: row * k in the outputs, or (kRowChunk)
+                       // the candidate-list offset from cand_val_off / cand_idx_off
+  int32_t n;           // keys to select from: visible keys (or key blocks when
+                       // block_len > 1; 0 for rows past a sequence's actual
+                       // length), a chunk's keys, or a split row's candidates
+  int32_t idx_offset;  // added to every returned index: output_idx_offset, or
+                       // (kRowChunk) the chunk's first key
+  int32_t row;         // output row (B*S1 rows for BSND, T1 for TND)
+  int32_t kind;        // RowKind
+};
+static_assert(sizeof(RowRec) == 32, "row record size");
 
 // Score-kernel variants: 8 waves of one query row each, arranged as WQ rows x
 // WK key slices; KT keys staged in LDS per step.
@@ -131,10 +160,13 @@ struct TopkArgs {
   const RowRec* rows;
   int32_t* out_idx;
   float* out_val;          // may be null
+  float* cand_val;         // candidate lists of split rows (workspace), or null
+  int32_t* cand_idx;
+  int64_t cand_val_off;    // workspace float offset of cand_val
   int32_t k;
   int32_t init_num;        // leading blocks of every row that are always returned
   int32_t local_num;       // trailing visible blocks of every row that are always returned
-  int32_t row_class[kTopkClasses + 1];   // class boundaries in rows (host copy)
+  int32_t row_class[2 * kTopkClasses + 1];   // pass / class boundaries in records (host copy)
 };
 
 // Host launchers (defined next to their kernels).

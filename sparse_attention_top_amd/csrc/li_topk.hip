@@ -33,6 +33,16 @@
 // with 11/11/10-bit digits (score first, index digits only on ties at the
 // threshold), compaction of the k winners into LDS and a bitonic sort.
 //
+// Split rows: where a problem has too few rows to fill the CUs, the host cuts
+// each long row into chunks of at most 8192 keys (each longer than k). A first
+// pass selects every chunk's top k (sorted, with values) into a candidate list
+// in the workspace, the chunks of a row side by side in key order; a second
+// pass selects the row's top k over its lists. The k largest composites of a
+// row are among its chunks' k largest, and equal scores in the lists stand in
+// key order (chunk order, then index order inside a chunk), so selecting on
+// list position and mapping the position back to the key gives the same
+// result as the whole row.
+//
 // Routing options of the ops-transformer issue's forward operator: the blocks
 // that are always kept (the first init_num and the last local_num of a row) are
 // written first, in ascending order, and the selection above runs over the
@@ -75,6 +85,21 @@ __device__ inline unsigned long long composite(float s, int j) {
 }
 
 __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFFFFFFFFu - (uint32_t)c); }
+
+// Where a record's result goes: output slots idx[d] / val[d] (val may be null).
+// A key's stored index is its position in the record's input, mapped through
+// gather when the input is a split row's candidate lists, plus off.
+struct Out {
+  int32_t* idx;
+  float* val;
+  const int32_t* gather;
+  int32_t off;
+  __device__ void put(uint32_t d, unsigned long long c) const {
+    const int32_t j = index_of(c);
+    idx[d] = (gather ? gather[j] : j) + off;
+    if (val) val[d] = from_ord((uint32_t)(c >> 32));
+  }
+};
 
 // W16: bucket counters are 16-bit halves of 32-bit words (rows of at most 65535
 // keys), else whole 32-bit words. The words are contiguous: a bucket's word
@@ -292,10 +317,10 @@ struct Row {
 };
 
 // Unused output slots [m, K): index -1, value -inf.
-__device__ inline void fill_tail(int m, int K, int32_t* oi, float* ov, int nt) {
+__device__ inline void fill_tail(int m, int K, const Out& out, int nt) {
   for (int e = m + (int)threadIdx.x; e < K; e += nt) {
-    oi[e] = -1;
-    if (ov) ov[e] = -__builtin_huge_valf();
+    out.idx[e] = -1;
+    if (out.val) out.val[e] = -__builtin_huge_valf();
   }
 }
 
@@ -303,7 +328,7 @@ __device__ inline void fill_tail(int m, int K, int32_t* oi, float* ov, int nt) {
 // The histogram words must be zero on entry.
 template <int NT, int R, bool RES, bool KEPT, bool W16, int KMAX>
 __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, float hi, int K, int m,
-                                  int32_t* oi, float* ov, int32_t ioff, Smem<NT, W16, KMAX>& sm) {
+                                  const Out& out, Smem<NT, W16, KMAX>& sm) {
   const int tid = threadIdx.x;
   const int n = row.count();
   const float range = hi - lo;
@@ -440,21 +465,17 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (s0[u] < s1[u] && !(bk[u] == t && rank[u] >= need)) {
-        const uint32_t d = s0[u] + rank[u];
-        oi[d] = index_of(me[u]) + ioff;
-        if (ov) ov[d] = from_ord((uint32_t)(me[u] >> 32));
-      }
+      if (s0[u] < s1[u] && !(bk[u] == t && rank[u] >= need)) out.put(s0[u] + rank[u], me[u]);
     }
   }
-  fill_tail(m, K, oi, ov, NT);
+  fill_tail(m, K, out, NT);
   return true;
 }
 
 // Fallback: exact radix select over the composite, then bitonic sort.
 template <int NT, int R, bool RES, bool KEPT, bool W16, int KMAX>
-__device__ void select_by_radix(const Row<NT, R, RES, KEPT>& row, int K, int m, int32_t* oi, float* ov,
-                                int32_t ioff, Smem<NT, W16, KMAX>& sm) {
+__device__ void select_by_radix(const Row<NT, R, RES, KEPT>& row, int K, int m, const Out& out,
+                                Smem<NT, W16, KMAX>& sm) {
   const int tid = threadIdx.x;
   const int n = row.count();
   uint32_t* cnt = sm.cnt;   // kRadixBins 32-bit counters
@@ -537,12 +558,8 @@ __device__ void select_by_radix(const Row<NT, R, RES, KEPT>& row, int K, int m, 
       __syncthreads();
     }
   }
-  for (int e = tid; e < m; e += NT) {
-    const unsigned long long cv = sm.buf[e];
-    oi[e] = index_of(cv) + ioff;
-    if (ov) ov[e] = from_ord((uint32_t)(cv >> 32));
-  }
-  fill_tail(m, K, oi, ov, NT);
+  for (int e = tid; e < m; e += NT) out.put(e, sm.buf[e]);
+  fill_tail(m, K, out, NT);
 }
 
 // One workgroup per row of one size class: row record first + blockIdx.x.
@@ -556,8 +573,14 @@ void topk_kernel(TopkArgs a, int first) {
   __shared__ Smem<NT, W16, KMAX> sm;
   const RowRec rr = a.rows[first + blockIdx.x];
   const int nb = rr.n;
-  int32_t* oi = a.out_idx + (int64_t)rr.row * a.k;
-  float* ov = a.out_val ? a.out_val + (int64_t)rr.row * a.k : nullptr;
+  Out out;
+  if (rr.kind == kRowChunk) {
+    out = Out{a.cand_idx + rr.out_off, a.cand_val + rr.out_off, nullptr, rr.idx_offset};
+  } else {
+    out = Out{a.out_idx + rr.out_off, a.out_val ? a.out_val + rr.out_off : nullptr,
+              rr.kind == kRowMerge ? a.cand_idx + (rr.ws_off - a.cand_val_off) : nullptr,
+              rr.idx_offset};
+  }
   const float* src = a.ws + rr.ws_off;
   int K = a.k;
   Row<NT, R, RES, KEPT> row;
@@ -572,11 +595,11 @@ void topk_kernel(TopkArgs a, int first) {
     const int kept = a1 + (nb - b0);
     for (int e = threadIdx.x; e < kept; e += NT) {
       const int j = e < a1 ? e : b0 + (e - a1);
-      oi[e] = j + rr.idx_offset;
-      if (ov) ov[e] = canon(src[j]);
+      out.idx[e] = j + out.off;
+      if (out.val) out.val[e] = canon(src[j]);
     }
-    oi += kept;
-    if (ov) ov += kept;
+    out.idx += kept;
+    if (out.val) out.val += kept;
     K -= kept;
     row.n = b0;
     row.lo_ = a1;
@@ -584,7 +607,7 @@ void topk_kernel(TopkArgs a, int first) {
   const int n = row.count();
   const int m = n < K ? n : K;
   if (m == 0) {
-    fill_tail(0, K, oi, ov, NT);
+    fill_tail(0, K, out, NT);
     return;
   }
   row.load();
@@ -598,11 +621,10 @@ void topk_kernel(TopkArgs a, int first) {
   });
   block_minmax<NT>(lo, hi, sm.s_red);
   const bool fast = (!W16 || n <= 65535) &&
-                    select_by_buckets<NT, R, RES, KEPT, W16, KMAX>(row, lo, hi, K, m, oi, ov,
-                                                                   rr.idx_offset, sm);
+                    select_by_buckets<NT, R, RES, KEPT, W16, KMAX>(row, lo, hi, K, m, out, sm);
   if (!fast) {
     __syncthreads();
-    select_by_radix<NT, R, RES, KEPT, W16, KMAX>(row, K, m, oi, ov, rr.idx_offset, sm);
+    select_by_radix<NT, R, RES, KEPT, W16, KMAX>(row, K, m, out, sm);
   }
 }
 
@@ -616,13 +638,19 @@ hipError_t launch_class(const TopkArgs& a, int c, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Both passes in order (the second reads the candidate lists the first wrote);
+// inside a pass one launch per non-empty class.
 template <int KMAX, bool KEPT>
 hipError_t launch_all(const TopkArgs& a, hipStream_t s) {
   hipError_t e;
-  if ((e = launch_class<256, 32, true, true, KMAX, KEPT>(a, 0, s)) != hipSuccess) return e;
-  if ((e = launch_class<512, 32, true, true, KMAX, KEPT>(a, 1, s)) != hipSuccess) return e;
-  if ((e = launch_class<1024, 32, true, true, KMAX, KEPT>(a, 2, s)) != hipSuccess) return e;
-  return launch_class<1024, 4, false, false, KMAX, KEPT>(a, 3, s);
+  for (int q = 0; q < 2; ++q) {
+    const int c0 = q * kTopkClasses;
+    if ((e = launch_class<256, 32, true, true, KMAX, KEPT>(a, c0, s)) != hipSuccess) return e;
+    if ((e = launch_class<512, 32, true, true, KMAX, KEPT>(a, c0 + 1, s)) != hipSuccess) return e;
+    if ((e = launch_class<1024, 32, true, true, KMAX, KEPT>(a, c0 + 2, s)) != hipSuccess) return e;
+    if ((e = launch_class<1024, 4, false, false, KMAX, KEPT>(a, c0 + 3, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <bool KEPT>

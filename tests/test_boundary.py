@@ -248,14 +248,18 @@ def _lengths(wl):
                           wl.cmp_residual_k, wl.output_idx_offset)
 
 
-def _row_table(wl, meta):
-    """Every output row appears once, with its visible-key count and the workspace
-    offset of its scores, in the size class of that count, longest first inside a
-    class."""
-    recs = B.parse_metadata(meta)[1]
+def _row_table(wl, meta, num_cus=256):
+    """Every output row is one record -- of the first pass, or, when split, of
+    the second pass with its chunks in the first -- carrying its visible-key
+    count, the workspace offset of its scores and its index offset; records sit
+    in the size class of their count, longest first inside a class; chunks tile
+    the row with 16-byte aligned starts and lengths in (k, 8192], and their
+    candidate lists lie side by side where the second-pass record reads them."""
+    h, recs, _ = B.parse_metadata(meta)
     rows, bounds = B.parse_row_table(meta)
-    assert bounds[0] == 0 and bounds[-1] == wl.num_rows and (np.diff(bounds) >= 0).all()
-    assert sorted(int(r) for r in rows["row"]) == list(range(wl.num_rows))
+    C, k = B.TOPK_CLASSES, wl.sparse_count
+    assert bounds[0] == 0 and bounds[-1] == len(rows) == int(h["num_recs"])
+    assert (np.diff(bounds) >= 0).all()
     where = {}
     for b in range(wl.B):
         nrows_b = (int(wl.cu_seqlens_q[b + 1]) - int(wl.cu_seqlens_q[b])
@@ -264,21 +268,62 @@ def _row_table(wl, meta):
             where[wl.row_of(b, i)] = (b, i)
     assert len(where) == wl.num_rows
     limits = (0,) + B.TOPK_CLASS_KEYS
-    for c in range(B.TOPK_CLASSES):
-        ns = []
-        for rec in rows[bounds[c]:bounds[c + 1]]:
-            row = int(rec["row"])
-            b, i = where[row]
-            L = max(1, wl.block_len)
-            n = -(-visible(wl, b, i) // L) if i < int(wl.seqlens_q[b]) else 0
-            assert int(rec["n"]) == n
-            off = 0 if wl.output_idx_offset is None else int(wl.output_idx_offset[b])
-            assert int(rec["idx_offset"]) == off
-            if n > 0:
-                assert int(rec["ws_off"]) == int(recs[b]["ws_off"]) + i * int(recs[b]["ld"])
-            assert (n == 0 and c == 0) or limits[c] < n <= limits[c + 1]
-            ns.append(n)
-        assert ns == sorted(ns, reverse=True)
+    split_ok = (k <= 2048 and wl.init_num == 0 and wl.local_num == 0
+                and wl.num_rows < 2 * num_cus)
+    seen, chunks = [], {}
+    cand_end = 0
+    for q in range(2):
+        for c in range(C):
+            ns = []
+            for rec in rows[bounds[q * C + c]:bounds[q * C + c + 1]]:
+                n, kind = int(rec["n"]), int(rec["kind"])
+                assert (n == 0 and c == 0) or limits[c] < n <= limits[c + 1]
+                ns.append(n)
+                if kind == B.ROW_CHUNK:
+                    assert q == 0
+                    chunks.setdefault(int(rec["row"]), []).append(rec)
+                    continue
+                assert kind == (B.ROW_WHOLE if q == 0 else B.ROW_MERGE)
+                row = int(rec["row"])
+                seen.append(row)
+                assert int(rec["out_off"]) == row * k
+                b, i = where[row]
+                L = max(1, wl.block_len)
+                nv = -(-visible(wl, b, i) // L) if i < int(wl.seqlens_q[b]) else 0
+                off = 0 if wl.output_idx_offset is None else int(wl.output_idx_offset[b])
+                assert int(rec["idx_offset"]) == off
+                row_ws = int(recs[b]["ws_off"]) + i * int(recs[b]["ld"])
+                if kind == B.ROW_WHOLE:
+                    assert n == nv and not (split_ok and n > 8192)
+                    if n > 0:
+                        assert int(rec["ws_off"]) == row_ws
+                    continue
+                assert split_ok and nv > 8192
+                ch = sorted(chunks.pop(row), key=lambda r: int(r["idx_offset"]))
+                nc = -(-nv // 8188)
+                assert len(ch) == nc and n == nc * k
+                starts = [int(r["idx_offset"]) for r in ch] + [nv]
+                assert starts[0] == 0 and all(x % 4 == 0 for x in starts[:-1])
+                lens = np.diff(starts)
+                assert (lens > k).all() and (lens <= 8192).all()
+                assert [int(r["n"]) for r in ch] == list(lens)
+                assert [int(r["ws_off"]) for r in ch] == [row_ws + x for x in starts[:-1]]
+                base = int(rec["ws_off"]) - int(h["cand_val_off"])
+                assert base % 4 == 0 and base >= 0
+                assert [int(r["out_off"]) for r in ch] == [base + j * k for j in range(nc)]
+                cand_end = max(cand_end, base + nc * k)
+            ns_sorted = sorted(ns, reverse=True)
+            assert ns == ns_sorted
+    assert not chunks, "chunks without a second-pass record"
+    assert sorted(seen) == list(range(wl.num_rows))
+    nsplit = int(h["split_rows"])
+    assert nsplit == sum(1 for r in rows if int(r["kind"]) == B.ROW_MERGE)
+    if nsplit:
+        vo, io = int(h["cand_val_off"]), int(h["cand_idx_off"])
+        scores_end = max(int(r["ws_off"]) + int(r["s_q"]) * int(r["ld"]) for r in recs)
+        assert vo >= scores_end and vo % 4 == 0
+        assert io - vo >= cand_end and int(h["ws_floats"]) >= io + cand_end
+    return nsplit
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -296,6 +341,35 @@ def test_metadata_covers_every_pair_once(lib, name):
         assert int(recs[b]["ws_off"]) % 4 == 0
     assert B.li_workspace_size(dp, meta) >= 4 * int(sum(int(r["s_q"]) * int(r["ld"])
                                                         for r in recs))
+
+
+def _split_wl(k=2048, rows=2, sk=30000, **kw):
+    return synth.build("sp", layout_q="TND", layout_k="TND", qk_dtype="bf16", w_dtype="bf16",
+                       N1=8, D=64, seqlens_q=[rows], seqlens_k=[sk], sparse_count=k,
+                       sparse_mode=0, seed=1, **kw)
+
+
+@pytest.mark.parametrize("case,cus,splits", [
+    (dict(), 256, 2),                                  # few long rows: split
+    (dict(sk=8192), 256, 0),                           # fits the first class: never split
+    (dict(sk=8193), 256, 2),
+    (dict(k=2049), 256, 0),                            # k above 2048: never split
+    (dict(block_len=4, init_num=1, local_num=1), 256, 0),   # kept blocks: never split
+    (dict(block_len=4, sk=40000), 256, 2),             # 10000 blocks per row: split
+    (dict(rows=600), 256, 0),                          # rows enough to fill the CUs
+    (dict(rows=600), 301, 600),                        # ... but not 301 of them
+    (dict(rows=2), 1, 0),
+])
+def test_split_decision(lib, case, cus, splits):
+    """Long rows are split only where rows are fewer than two per CU, k <= 2048
+    and no blocks are always kept; the table stays consistent either way."""
+    wl = _split_wl(**case)
+    meta = B.li_metadata(I.problem_of(wl), _lengths(wl), cus)
+    assert _row_table(wl, meta, cus) == splits
+    h = B.parse_metadata(meta)[0]
+    if splits:
+        assert B.li_workspace_size(I.problem_of(wl), meta) == 4 * int(h["ws_floats"])
+        assert int(h["cand_idx_off"]) > int(h["cand_val_off"]) > 0
 
 
 def test_metadata_heaviest_first_and_balanced(lib):

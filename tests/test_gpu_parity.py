@@ -399,6 +399,58 @@ def test_work_decomposition_does_not_change_results(name):
         assert torch.equal(idx, outs[0][0]) and torch.equal(val, outs[0][1])
 
 
+SPLIT_CASES = {
+    # chunk counts 2, 2, 3, 5, 9 and 25 (a second pass in every thread count)
+    "tnd_bf16_lengths": dict(layout_q="TND", layout_k="TND", qk_dtype="bf16", w_dtype="bf16",
+                             N1=16, D=64, seqlens_q=[1, 1, 1, 2, 1, 1],
+                             seqlens_k=[8193, 16376, 16377, 40000, 70000, 200000],
+                             sparse_count=2048, sparse_mode=0),
+    "paged_offsets_causal": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16",
+                                 w_dtype="f32", N1=64, D=128, seqlens_q=[2, 2, 2],
+                                 seqlens_k=[9000, 30000, 65536], block_size=128,
+                                 sparse_count=512, sparse_mode=3, output_idx_offset=[0, 9000, 7]),
+    "fp8_k1": dict(layout_q="TND", layout_k="TND", qk_dtype="e4m3fn", w_dtype="f32", N1=32,
+                   D=128, seqlens_q=[2, 1], seqlens_k=[30000, 12000], sparse_count=1,
+                   sparse_mode=3),
+    "blocks_l2": dict(layout_q="TND", layout_k="TND", qk_dtype="f16", w_dtype="f32", N1=8,
+                      D=64, seqlens_q=[1, 2], seqlens_k=[50000, 17000], sparse_count=300,
+                      sparse_mode=3, block_len=2),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_split_rows_match_whole_rows(name):
+    """Long rows of a problem with few rows are split into chunks whose top-k
+    lists a second pass merges. The result passes the oracle's rule and is
+    bit-identical to the unsplit path (one CU's worth of rows never splits)."""
+    wl = synth.build(f"split_{name}", seed=31, **SPLIT_CASES[name])
+    st, idx, val = run_and_check(wl, label=f"split_{name}")
+    plan = I.run_workload(wl, DEV, return_value=True)[2]
+    assert int(plan.header["split_rows"]) > 0
+    i1, v1, plan1, _ = I.run_workload(wl, DEV, return_value=True, num_cus=1)
+    assert int(plan1.header["split_rows"]) == 0
+    assert torch.equal(idx, i1) and torch.equal(val, v1)
+
+
+@pytest.mark.parametrize("sk", [8193, 40000, 100000])
+def test_split_rows_with_equal_scores(sk):
+    """All scores 0: every chunk and the merge take the exact fallback, and the
+    merge orders equal scores by key index across chunk boundaries."""
+    k = 2048
+    wl = synth.build("split_zero", layout_q="TND", layout_k="TND", qk_dtype="bf16",
+                     w_dtype="f32", N1=8, D=64, seqlens_q=[2], seqlens_k=[sk], sparse_count=k,
+                     sparse_mode=0, output_idx_offset=[5], seed=13)
+    wl.w = np.zeros_like(wl.w)
+    _say(f"[gpu] split rows, zero weights sk={sk}")
+    idx, val, plan, _ = I.run_workload(wl, DEV, return_value=True)
+    assert int(plan.header["split_rows"]) == 2
+    gi = idx.cpu().numpy().reshape(2, k)
+    gv = val.cpu().numpy().reshape(2, k)
+    for i in range(2):
+        assert gi[i].tolist() == list(range(5, 5 + k))
+        assert (gv[i] == 0).all() and not np.signbit(gv[i]).any()
+
+
 def test_values_flag_does_not_change_indices():
     wl = synth.test_shape(S1=64, S2=900, sparse_count=200)
     i1, _, _, _ = I.run_workload(wl, DEV, return_value=False)
