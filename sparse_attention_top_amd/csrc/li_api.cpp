@@ -426,6 +426,16 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     LI_CHECK(covered == nrows, LI_ERR_INVALID_ARGUMENT,
              "sequences cover %lld output rows, the problem has %lld", (long long)covered,
              (long long)nrows);
+    // The second pass is short (one record per split row) and runs alone: one
+    // launch, in the class of its longest record, instead of one per class.
+    for (int c = kTopkClasses - 1; c > 0; --c) {
+      if (pass[1][c].empty()) continue;
+      for (int d = 0; d < c; ++d) {
+        pass[1][c].insert(pass[1][c].end(), pass[1][d].begin(), pass[1][d].end());
+        pass[1][d].clear();
+      }
+      break;
+    }
     const int64_t cand_idx_off = cand_val_off + cand;
     if (cand > 0) ws = cand_idx_off + cand;
     int64_t nrecs = 0;

@@ -251,8 +251,9 @@ def _lengths(wl):
 def _row_table(wl, meta, num_cus=256):
     """Every output row is one record -- of the first pass, or, when split, of
     the second pass with its chunks in the first -- carrying its visible-key
-    count, the workspace offset of its scores and its index offset; records sit
-    in the size class of their count, longest first inside a class; chunks tile
+    count, the workspace offset of its scores and its index offset; first-pass
+    records sit in the size class of their count, second-pass records all in
+    the class of the longest, longest first inside a class; chunks tile
     the row with 16-byte aligned starts and lengths in (k, 8192], and their
     candidate lists lie side by side where the second-pass record reads them."""
     h, recs, _ = B.parse_metadata(meta)
@@ -277,7 +278,11 @@ def _row_table(wl, meta, num_cus=256):
             ns = []
             for rec in rows[bounds[q * C + c]:bounds[q * C + c + 1]]:
                 n, kind = int(rec["n"]), int(rec["kind"])
-                assert (n == 0 and c == 0) or limits[c] < n <= limits[c + 1]
+                if q == 0:
+                    assert (n == 0 and c == 0) or limits[c] < n <= limits[c + 1]
+                else:   # one launch: every record in the class of the longest
+                    assert n <= limits[c + 1] and (ns or limits[c] < n)
+                    assert all(bounds[C + d] == bounds[C + d + 1] for d in range(C) if d != c)
                 ns.append(n)
                 if kind == B.ROW_CHUNK:
                     assert q == 0
