@@ -330,7 +330,9 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     const int64_t whole = std::max<int64_t>(KT, ((int64_t)max_sk + KT - 1) / KT * KT);
     int64_t chunk = whole;
     if (tiles < 2ll * num_cus) {
-      const int64_t target_items = 4ll * num_cus;
+      // Four items per CU (eight for decode, whose items are short and run two
+      // per CU): fewer leave a tail, more repeat the query loads.
+      const int64_t target_items = (variant == kVarDecode ? 8ll : 4ll) * num_cus;
       chunk = (pairs + TQ * target_items - 1) / (TQ * target_items);
       chunk = std::max<int64_t>(chunk, 8ll * KT);
       chunk = std::min<int64_t>((chunk + KT - 1) / KT * KT, whole);

@@ -118,15 +118,18 @@ struct RowRec {
 };
 static_assert(sizeof(RowRec) == 32, "row record size");
 
-// Score-kernel variants: 8 waves of one query row each, arranged as WQ rows x
-// WK key slices; KT keys staged in LDS per step.
+// Score-kernel variants: waves of one query row each, arranged as WQ rows x WK
+// key slices; KT keys staged in LDS per step. Prefill workgroups have 8 waves
+// (one per CU); the short-sequence ones have 4 and run two per CU, so that one
+// workgroup's start (query loads, first stages) overlaps the other's key loop.
 enum ScoreVariant : int32_t {
   kVarPrefill = 0,  // WQ=8, WK=1: 8 query rows share each staged key tile
-  kVarMid = 1,      // WQ=4, WK=2: 4 query rows
-  kVarDecode = 2,   // WQ=2, WK=4: 2 query rows, waves split the keys
+  kVarMid = 1,      // WQ=4, WK=1: 4 query rows
+  kVarDecode = 2,   // WQ=2, WK=2: 2 query rows, two waves per row split the keys
 };
 constexpr int kVariantTileQ[3] = {8, 4, 2};
-constexpr int kVariantTileK[3] = {128, 128, 256};
+constexpr int kVariantWaves[3] = {8, 4, 4};
+constexpr int kVariantTileK[3] = {128, 128, 128};
 
 // ---------------------------------------------------------------------------
 // Kernel arguments

@@ -11,9 +11,11 @@
 //
 // Work decomposition (one workgroup per work item of the task table):
 //   * the workgroup owns WQ query rows of one sequence and a key range [k0,k1);
-//   * 8 waves (two per SIMD, so one can issue while the other waits) = WQ rows x
-//     WK key slices; a wave holds its row's query heads in VGPRs as MFMA
-//     A-operands for the whole key loop;
+//   * WQ rows x WK key slices of waves, two waves per SIMD so that one can issue
+//     while the other waits: 8 waves in one workgroup per CU for prefill tiles,
+//     4 waves in each of two workgroups per CU for short sequences (one
+//     workgroup's start then overlaps the other's key loop); a wave holds its
+//     row's query heads in VGPRs as MFMA A-operands for the whole key loop;
 //   * keys are staged KT at a time in two LDS buffers by direct global -> LDS
 //     loads (no staging registers), gathered through the block table for the
 //     paged layout;
@@ -170,7 +172,7 @@ template <int N> __device__ inline void stage_barrier() {
 // BL: store one score per block of block_len keys (the block maximum) instead
 // of one per key.
 template <int DT, int D, int NT, int WQ, int WK, int KT, bool BL>
-__global__ __launch_bounds__(WQ * WK * 64) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kernel(ScoreArgs a) {
   using M = Mma<DT>;
   using Frag = typename M::Frag;
   using Acc = typename M::Acc;
@@ -489,15 +491,15 @@ hipError_t launch_v(int variant, int num_items, const ScoreArgs& a, hipStream_t 
   switch (variant) {
     case kVarPrefill:
       hipLaunchKernelGGL((score_kernel<DT, D, NT, 8, 1, kVariantTileK[kVarPrefill], BL>),
-                         dim3(num_items), dim3(512), 0, s, a);
+                         dim3(num_items), dim3(64 * kVariantWaves[kVarPrefill]), 0, s, a);
       break;
     case kVarMid:
-      hipLaunchKernelGGL((score_kernel<DT, D, NT, 4, 2, kVariantTileK[kVarMid], BL>),
-                         dim3(num_items), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((score_kernel<DT, D, NT, 4, 1, kVariantTileK[kVarMid], BL>),
+                         dim3(num_items), dim3(64 * kVariantWaves[kVarMid]), 0, s, a);
       break;
     case kVarDecode:
-      hipLaunchKernelGGL((score_kernel<DT, D, NT, 2, 4, kVariantTileK[kVarDecode], BL>),
-                         dim3(num_items), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((score_kernel<DT, D, NT, 2, 2, kVariantTileK[kVarDecode], BL>),
+                         dim3(num_items), dim3(64 * kVariantWaves[kVarDecode]), 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;
