@@ -185,7 +185,9 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
   constexpr int STAGE = KT * ROW;          // bytes of one staged key tile
   constexpr int DMA = STAGE / 1024;        // 1 KB wave loads per stage
   constexpr int DPW = DMA / NW;            // ... per wave
-  constexpr int U = ROW / LB;              // swizzle units per key row
+  constexpr int U = ROW / 16;              // 16-byte swizzle units per key row
+  constexpr int LOG_U = __builtin_ctz(U);
+  constexpr int NU = LB / 16;              // units per lane fragment (1 or 2)
   constexpr int RPW = ROW >= 128 ? 1 : 128 / ROW;   // key rows per 128-byte bank window
   constexpr bool QUANT = (DT == LI_DTYPE_E4M3FN) || (DT == LI_DTYPE_I8);
   constexpr int SPS = KT / 32 / WK;        // 32-key slices per staged tile per wave
@@ -193,15 +195,20 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
   static_assert(KT % (32 * WK) == 0 && SPS % 2 == 0, "a stage holds an even number of slices");
   static_assert(KSTEPS >= 1 && ROW % (2 * LB) == 0, "head dim must fill whole k-steps");
   static_assert(STAGE % (1024 * NW) == 0, "every wave stages the same number of 1 KB blocks");
-  static_assert((ROW & (ROW - 1)) == 0 && (U & (U - 1)) == 0, "power-of-two rows");
+  static_assert((ROW & (ROW - 1)) == 0 && (U & (U - 1)) == 0 && NU * 16 == LB, "power-of-two rows");
   static_assert(!QUANT || KT <= NTHR, "one thread per staged key scale");
 
   // Two staged key tiles. Key row r of a tile occupies bytes [r*ROW, (r+1)*ROW);
-  // its LB-byte unit u is stored at unit position u ^ swz(r), so that the 32
-  // rows read together by a B-fragment load spread over all LDS banks.
+  // its 16-byte unit u is stored at unit position u ^ swz(r). A fragment read
+  // is one or two 16-byte LDS reads per lane, each taking the same unit of 32
+  // consecutive rows; with x = r / RPW, swz = (x ^ (x >> log2 U)) mod U puts
+  // any 8 (and any 16) consecutive rows of such a read on distinct banks.
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2 * STAGE];
   __shared__ float ksc[2][QUANT ? KT : 1];
-  auto swz = [](int r) { return (r / RPW) & (U - 1); };
+  auto swz = [](int r) {
+    const int x = r / RPW;
+    return (x ^ (x >> LOG_U)) & (U - 1);
+  };
 
   const WorkItem it = a.items[blockIdx.x];
   const BatchRec br = a.batches[it.b];
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
   auto dma_byte = [&](int d) {
     const int r = dma_row(d);
     const int b = (lane * 16) % ROW;   // 1 KB blocks hold whole rows
-    return (((b / LB) ^ swz(r)) * LB) + (b % LB);
+    return ((b / 16) ^ swz(r)) * 16;
   };
   auto stage_key = [&](int st, int kk) { return min(it.k0 + st * KT + kk, jmax); };
   auto block_index = [&](int j) { return a.block_shift >= 0 ? j >> a.block_shift : j / a.block_size; };
@@ -372,14 +379,21 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
   // vector-memory operations before each barrier are exactly SPS stores.
   auto slice_key = [&](int st, int i) { return it.k0 + st * KT + (wk + i * WK) * 32; };
   // LDS byte address of this lane's B fragment of k-step s in slice (buf, sub):
-  // frag_base(buf, sub) ^ (2*LB*s), rows being ROW-aligned.
+  // logical units (2s + half)*NU + e (e < NU) of row r, i.e. the addresses
+  // frag_base(buf, sub) ^ (2*LB*s) ^ (16*e), rows being ROW-aligned.
   auto frag_base = [&](int buf, int sub) {
     const int r = sub * 32 + col;
-    const int x = swz(r);
-    return buf * STAGE + r * ROW + LB * (half ^ (x & 1)) + 2 * LB * (x >> 1);
+    return buf * STAGE + r * ROW + 16 * ((half * NU) ^ swz(r));
   };
   auto read_frag = [&](int base, int s) {
-    return *reinterpret_cast<const Frag*>(&kbuf[base ^ (2 * LB * s)]);
+    const int a = base ^ (2 * LB * s);
+    if constexpr (NU == 1) {
+      return *reinterpret_cast<const Frag*>(&kbuf[a]);
+    } else {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(&kbuf[a]);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(&kbuf[a ^ 16]);
+      return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
   };
   Frag bf[KSTEPS];
   {
