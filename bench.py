@@ -11,9 +11,15 @@ right-down causal, BSND); the other seeded workloads can be selected with
 Prints ONE JSON line. `value` is indexed query tokens per second; the line
 also carries the score kernel's TFLOP/s against the MFMA peak (or its GB/s
 against HBM when the workload is bandwidth-bound), the top-k kernel's GB/s,
-a `roofline` object for the dominant kernel (timed with HIP events on the
-stream it runs on) and a `cpu_baseline` object: the fp64 CPU oracle timed on a
-bounded random sample of the same rows on this host.
+a `roofline` object for the dominant kernel and a `cpu_baseline` object: the
+fp64 CPU oracle timed on a bounded random sample of the same rows on this host.
+
+Timing: after W eager warmup steps, K steps (li_score + li_topk each) are
+captured as one HIP graph, replayed once untimed and once between two HIP
+events on the stream it runs on (ms_per_step = elapsed / K); K launches of the
+score kernel alone and of the top-k alone are timed the same way (score_ms,
+topk_ms, and the roofline's achieved rate). --eager times K eagerly launched
+steps instead.
 """
 import argparse
 import hashlib
@@ -86,6 +92,8 @@ def main():
     ap.add_argument("--return-value", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step eagerly instead of replaying captured graphs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -118,40 +126,74 @@ def main():
     val = torch.empty(shape if p.return_value else (0,), dtype=torch.float32, device=dev)
     inp = dw.inputs()
     stream = torch.cuda.current_stream()
-    sh = int(stream.cuda_stream)
     mh, md, ws, wsb = plan.meta_host, int(plan.meta_dev.data_ptr()), int(plan.ws.data_ptr()), \
         plan.ws_bytes
     ip, vp = int(idx.data_ptr()), (int(val.data_ptr()) if p.return_value else 0)
 
+    def cur():
+        return int(torch.cuda.current_stream().cuda_stream)
+
     def score():
-        B.li_score(p, inp, mh, md, ws, wsb, sh)
+        B.li_score(p, inp, mh, md, ws, wsb, cur())
 
     def topk():
-        B.li_topk(p, mh, md, ws, wsb, ip, vp, sh)
+        B.li_topk(p, mh, md, ws, wsb, ip, vp, cur())
 
-    for _ in range(args.warmup):
+    def step():
         score()
         topk()
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", flush=True, file=sys.stderr)
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(K):
-        ev[s][0].record(stream)
-        score()
-        ev[s][1].record(stream)
-        topk()
-        ev[s][2].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    score_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    topk_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    ms_per_step = total_ms / K
+    if args.eager:
+        # Launch by launch, HIP events between the kernels of every step.
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for s in range(K):
+            ev[s][0].record(stream)
+            score()
+            ev[s][1].record(stream)
+            topk()
+            ev[s][2].record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = start.elapsed_time(end) / K
+        score_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+        topk_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    else:
+        # K steps (and K launches of each kernel alone) captured as one HIP
+        # graph each and replayed once between two HIP events on the stream
+        # it runs on: the timed region then holds GPU work only (eager
+        # launches through ctypes leave host gaps that short workloads feel).
+        graphs = {}
+        for name, fn in (("step", step), ("score", score), ("topk", topk)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(K):
+                    fn()
+            graphs[name] = g
+        torch.cuda.synchronize()
+
+        def timed(g):
+            g.replay()   # one untimed replay (graph upload)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / K
+
+        ms_per_step = timed(graphs["step"])
+        score_ms = timed(graphs["score"])
+        topk_ms = timed(graphs["topk"])
+        del graphs
     print(f"[bench] timed {K} steps: {ms_per_step:.3f} ms/step (score {score_ms:.3f}, "
           f"top-k {topk_ms:.3f})", flush=True, file=sys.stderr)
 
