@@ -197,17 +197,46 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
   static_assert(STAGE % (1024 * NW) == 0, "every wave stages the same number of 1 KB blocks");
   static_assert((ROW & (ROW - 1)) == 0 && (U & (U - 1)) == 0 && NU * 16 == LB, "power-of-two rows");
   static_assert(!QUANT || KT <= NTHR, "one thread per staged key scale");
+  // Query rows of 256-byte heads (16-bit D = 128) are staged through LDS when
+  // they fit beside one key stage (160 KB for one workgroup per CU, 80 KB for
+  // two): QROW bytes per row (N1 <= 64). Loaded straight into A-operand
+  // registers, each 1 KB load of a row touches 32 cache lines (32 bytes of 32
+  // heads); staged, it is one coalesced 1 KB block. (Shorter heads gained
+  // nothing measurable and keep the direct loads.)
+  constexpr int QROW = 64 * ROW;
+  constexpr int LDS_CAP = NW == 8 ? 160 * 1024 : 80 * 1024;
+  constexpr int QEXTRA = QUANT ? 2 * KT * 4 : 0;
+  constexpr bool QLDS = ROW >= 256 && STAGE + WQ * QROW + QEXTRA <= LDS_CAP;
+  // The query rows sit after both key stages if they fit there, else over the
+  // second stage (which is then loaded once they have been read).
+  constexpr bool QOVER = 2 * STAGE + WQ * QROW + QEXTRA > LDS_CAP;
+  constexpr int QOFF = QOVER ? STAGE : 2 * STAGE;
+  constexpr int KBUF = QLDS ? (QOFF + WQ * QROW > 2 * STAGE ? QOFF + WQ * QROW : 2 * STAGE)
+                            : 2 * STAGE;
 
   // Two staged key tiles. Key row r of a tile occupies bytes [r*ROW, (r+1)*ROW);
   // its 16-byte unit u is stored at unit position u ^ swz(r). A fragment read
   // is one or two 16-byte LDS reads per lane, each taking the same unit of 32
   // consecutive rows; with x = r / RPW, swz = (x ^ (x >> log2 U)) mod U puts
   // any 8 (and any 16) consecutive rows of such a read on distinct banks.
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[KBUF];
   __shared__ float ksc[2][QUANT ? KT : 1];
   auto swz = [](int r) {
     const int x = r / RPW;
     return (x ^ (x >> LOG_U)) & (U - 1);
+  };
+
+  // The LB-byte fragment at LDS byte base ^ (2*LB*s) (and ^16 for its second
+  // 16-byte half).
+  auto read_frag = [&](int base, int s) {
+    const int a = base ^ (2 * LB * s);
+    if constexpr (NU == 1) {
+      return *reinterpret_cast<const Frag*>(&kbuf[a]);
+    } else {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(&kbuf[a]);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(&kbuf[a ^ 16]);
+      return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
   };
 
   const WorkItem it = a.items[blockIdx.x];
@@ -296,27 +325,46 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
   const int nstages = (it.k1 - it.k0 + KT - 1) / KT;
   ids(0);
   fetch(0);
-  stash_scales(0);
-  if (nstages > 1) {
-    ids(1);
-    fetch(1);
-  }
-  if (nstages > 2) ids(2);
-
-  // Query heads of this row as MFMA A-operands (zero for padded heads), and the
-  // per-lane weights of the 16 heads each lane accumulates per tile. Every load
-  // is unconditional (clamped index, masked afterwards) so that they are all in
-  // flight together with the first key tiles.
+  if (!(QLDS && QOVER)) stash_scales(0);
   Frag qf[NT][KSTEPS];
+  if constexpr (QLDS) {
+    // The row's N1 x ROW query bytes go to LDS as coalesced 1 KB blocks (split
+    // over the row's WK waves), head h laid out like key row h, and come back
+    // as A-operands with the key fragments' conflict-free reads. Bytes past the
+    // row's heads (clamped source) land in padded heads, which are masked.
+    const int qbytes = a.n1 * ROW;
+    const uint8_t* qsrc = a.q + qrow * (int64_t)qbytes;
+    const uint32_t qlds = lds0 + QOFF + wq * QROW;
+    for (int bk = wk; bk * 1024 < qbytes; bk += WK) {
+      const int L = bk * 1024 + lane * 16;
+      const int h = L / ROW;
+      const int g = h * ROW + (((L % ROW) / 16) ^ swz(h)) * 16;
+      lds_dma16(qsrc + (g < qbytes ? g : qbytes - 16), qlds + bk * 1024);
+    }
+  } else {
+    if (nstages > 1) {
+      ids(1);
+      fetch(1);
+    }
+    // Query heads of this row as MFMA A-operands (zero for padded heads). Every
+    // load is unconditional (clamped index, masked afterwards) so that they are
+    // all in flight together with the first key tiles.
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int h = 32 * t + col;
-    const bool ok = row_ok && h < a.n1;
-    const uint8_t* src = a.q + ((qrow * a.n1 + (ok ? h : 0)) * D) * ES + half * LB;
-    const int mask = ok ? -1 : 0;
+    for (int t = 0; t < NT; ++t) {
+      const int h = 32 * t + col;
+      const bool ok = row_ok && h < a.n1;
+      const uint8_t* src = a.q + ((qrow * a.n1 + (ok ? h : 0)) * D) * ES + half * LB;
+      const int mask = ok ? -1 : 0;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[t][s] = load_frag<Frag>(src + s * 2 * LB) & mask;
+      for (int s = 0; s < KSTEPS; ++s) qf[t][s] = load_frag<Frag>(src + s * 2 * LB) & mask;
+    }
   }
+  if (QLDS && nstages > 1) {
+    ids(1);
+    if (!QOVER) fetch(1);
+  }
+  if (!(QLDS && QOVER) && nstages > 2) ids(2);
+  // The per-lane weights of the 16 heads each lane accumulates per tile.
   float wr[NT][16];
   {
     int64_t widx[NT][16];
@@ -365,7 +413,25 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
         wr[t][e] = (row_ok && he < a.n1) ? wr[t][e] : 0.f;
       }
   }
-  stage_barrier<0>();   // stage 0 (and 1) staged, query and weights in registers
+  if constexpr (QLDS) {
+    stage_barrier<0>();   // stage 0 (and 1) and the query rows staged, weights in registers
+    if (QOVER) stash_scales(0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int h = 32 * t + col;
+      const int mask = (row_ok && h < a.n1) ? -1 : 0;
+      const int qb = QOFF + wq * QROW + h * ROW + 16 * ((half * NU) ^ swz(h));
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[t][s] = read_frag(qb, s) & mask;
+    }
+    if constexpr (QOVER) {
+      stage_barrier<0>();   // query rows read (their space takes stage 1), scales published
+      if (nstages > 1) fetch(1);
+      if (nstages > 2) ids(2);
+    }
+  } else {
+    stage_barrier<0>();   // stage 0 (and 1) staged, query and weights in registers
+  }
 
   // One loop iteration per stage, its SPS slices unrolled. Slice i of stage st
   // covers keys [k0 + st*KT + (wk + i*WK)*32, +32) in buffer st & 1. Before the
@@ -384,16 +450,6 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
   auto frag_base = [&](int buf, int sub) {
     const int r = sub * 32 + col;
     return buf * STAGE + r * ROW + 16 * ((half * NU) ^ swz(r));
-  };
-  auto read_frag = [&](int base, int s) {
-    const int a = base ^ (2 * LB * s);
-    if constexpr (NU == 1) {
-      return *reinterpret_cast<const Frag*>(&kbuf[a]);
-    } else {
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(&kbuf[a]);
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(&kbuf[a ^ 16]);
-      return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
   };
   Frag bf[KSTEPS];
   {
