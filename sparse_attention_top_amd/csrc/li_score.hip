@@ -15,7 +15,9 @@
 //     while the other waits: 8 waves in one workgroup per CU for prefill tiles,
 //     4 waves in each of two workgroups per CU for short sequences (one
 //     workgroup's start then overlaps the other's key loop); a wave holds its
-//     row's query heads in VGPRs as MFMA A-operands for the whole key loop;
+//     row's query heads in VGPRs as MFMA A-operands for the whole key loop
+//     (16-bit D = 128 rows arrive through LDS as coalesced blocks, others by
+//     direct loads);
 //   * keys are staged KT at a time in two LDS buffers by direct global -> LDS
 //     loads (no staging registers), gathered through the block table for the
 //     paged layout;
