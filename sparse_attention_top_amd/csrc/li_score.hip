@@ -416,7 +416,7 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
       }
   }
   if constexpr (QLDS) {
-    stage_barrier<0>();   // stage 0 (and 1) and the query rows staged, weights in registers
+    stage_barrier<0>();   // stage 0 (and 1 if apart from the rows), rows staged, weights in registers
     if (QOVER) stash_scales(0);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
