@@ -187,6 +187,18 @@ EDGE = {
     "blocks_k4096": dict(layout_q="TND", layout_k="TND", qk_dtype="bf16", w_dtype="bf16", N1=16,
                          D=64, seqlens_q=[3, 2], seqlens_k=[9000, 40000], sparse_count=4096,
                          sparse_mode=3, block_len=2, init_num=16, local_num=64),
+    # query rows staged through LDS (16-bit, D = 128) with head counts that leave
+    # a partial 1 KB block and padded heads: prefill tiles, 4-row tiles, decode
+    "lds_query_n3_prefill": dict(layout_q="BSND", layout_k="BSND", qk_dtype="bf16",
+                                 w_dtype="f32", N1=3, D=128, seqlens_q=[300], seqlens_k=[300],
+                                 sparse_count=40, sparse_mode=3),
+    "lds_query_n5_mid": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="f16", w_dtype="bf16",
+                             N1=5, D=128, seqlens_q=[4, 3], seqlens_k=[2000, 700],
+                             block_size=64, sparse_count=100, sparse_mode=3),
+    "lds_query_n37_decode": dict(layout_q="BSND", layout_k="PA_BSND", qk_dtype="bf16",
+                                 w_dtype="f16", N1=37, D=128, seqlens_q=[2, 1, 2],
+                                 seqlens_k=[3000, 64, 5000], block_size=128, sparse_count=256,
+                                 sparse_mode=3),
 }
 
 
