@@ -9,7 +9,8 @@
 // wanted set is exactly the k largest composites and the wanted order is
 // descending composite order. Every composite is > 0.
 //
-// One workgroup per output row. Rows are grouped by the host into size classes
+// One workgroup per top-k record: an output row (or, for split rows below, one
+// chunk of a row or one row's chunk lists). Records are grouped by the host into size classes
 // (up to 8K, 16K, 32K visible keys, longer), each class sorted longest first so
 // that short rows fill the tail of its launch; a class runs a kernel whose NT
 // threads keep the row in registers (R scores per thread, loaded as float4) or,
@@ -562,7 +563,8 @@ __device__ void select_by_radix(const Row<NT, R, RES, KEPT>& row, int K, int m, 
   fill_tail(m, K, out, NT);
 }
 
-// One workgroup per row of one size class: row record first + blockIdx.x.
+// One workgroup per record of one size class: record first + blockIdx.x; the
+// record's kind says where its scores come from and where its result goes.
 // W16 (16-bit bucket counters) is used only for rows of at most 65535 keys.
 // A row's latency is a chain of dependent LDS and memory steps, so throughput
 // comes from rows in flight: the 256-thread kernel (every row up to 8K keys, in
