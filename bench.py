@@ -149,7 +149,27 @@ def main():
     print(f"[bench] warmup done ({args.warmup} steps)", flush=True, file=sys.stderr)
 
     K = args.steps
-    if args.eager:
+    timing = "eager" if args.eager else "graph"
+    if not args.eager:
+        # K steps (and K launches of each kernel alone) captured as one HIP
+        # graph each and replayed once between two HIP events on the stream
+        # it runs on: the timed region then holds GPU work only (eager
+        # launches through ctypes leave host gaps that short workloads feel).
+        try:
+            graphs = {}
+            for name, fn in (("step", step), ("score", score), ("topk", topk)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(K):
+                        fn()
+                graphs[name] = g
+            torch.cuda.synchronize()
+        except RuntimeError as e:   # capture unavailable: time eager launches instead
+            print(f"[bench] graph capture failed ({e}); timing eager launches", flush=True,
+                  file=sys.stderr)
+            timing = "eager"
+            torch.cuda.synchronize()
+    if timing == "eager":
         # Launch by launch, HIP events between the kernels of every step.
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -167,19 +187,6 @@ def main():
         score_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
         topk_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
     else:
-        # K steps (and K launches of each kernel alone) captured as one HIP
-        # graph each and replayed once between two HIP events on the stream
-        # it runs on: the timed region then holds GPU work only (eager
-        # launches through ctypes leave host gaps that short workloads feel).
-        graphs = {}
-        for name, fn in (("step", step), ("score", score), ("topk", topk)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for _ in range(K):
-                    fn()
-            graphs[name] = g
-        torch.cuda.synchronize()
-
         def timed(g):
             g.replay()   # one untimed replay (graph upload)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -253,7 +260,7 @@ def main():
                    "N2": wl.N2, "D": wl.D, "layout_q": wl.layout_q, "layout_k": wl.layout_k,
                    "sparse_count": kk, "sparse_mode": wl.sparse_mode,
                    "return_value": bool(p.return_value), "query_rows": rows,
-                   "visible_pairs": pairs, "parallelism": "single GPU"},
+                   "visible_pairs": pairs, "parallelism": "single GPU", "timing": timing},
         "score_tflops": round(score_tflops, 1),
         "score_frac_mfma_peak": round(score_tflops / peak_mfma, 4),
         "score_ms": round(score_ms, 4),
