@@ -442,9 +442,10 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
   // earlier) the stage after next is loaded into it. Per slice: MFMAs of the
   // slice, each k-step's B fragment reloaded right after use with the next
   // slice's, and the ReLU / weight / in-lane head reduction of the previous
-  // slice interleaved between the MFMAs; then the cross-half swap-add and the
-  // store of that previous slice. The store has no branch, so the last SPS
-  // vector-memory operations before each barrier are exactly SPS stores.
+  // slice interleaved between the MFMAs; every second slice, the cross-half
+  // swap-add and the store of the two previous slices. The store has no branch,
+  // so the vector-memory operations issued after the last key DMA before each
+  // barrier are exactly SPS/2 stores (SPS/2 - 1 in the first stage).
   auto slice_key = [&](int st, int i) { return it.k0 + st * KT + (wk + i * WK) * 32; };
   // LDS byte address of this lane's B fragment of k-step s in slice (buf, sub):
   // logical units (2s + half)*NU + e (e < NU) of row r, i.e. the addresses
@@ -530,28 +531,56 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
     }
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rsrc, off, 0, 0);
   };
+  // Two slices at once: one swap leaves slice A's totals in the lower half-wave
+  // and slice B's in the upper one (each added in the same order as above), and
+  // one store writes both.
+  auto finish2 = [&](float pa, int kba, float ksa, bool valida, float pb, int kbb, float ksb) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb),
+                                                     false, false);
+    float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (QUANT) tot *= half ? ksb : ksa;
+    const int kb = half ? kbb : kba;
+    const bool valid = half ? true : valida;
+    int off;
+    if constexpr (BL) {
+      const int j = kb + col;
+      tot = group_max(j < lim ? tot : -__builtin_huge_valf(), a.key_block);
+      off = (valid && (col & (a.key_block - 1)) == 0) ? (j >> a.key_block_shift) * 4 : kDropOffset;
+    } else {
+      off = valid ? (kb + col) * 4 : kDropOffset;
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rsrc, off, 0, 0);
+  };
 
   Acc acc0[NT], acc1[NT];   // even slices of a stage accumulate in acc0, odd in acc1
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc1[t] = M::zero();   // read by slice 0's (dropped) epilogue
   float ks0 = 1.f, ks1 = 1.f;
+  float hp = 0.f, hks = 1.f;   // an even slice's part, finished with the next one
+  int hkb = 0;
+  bool hvalid = false;
   for (int st = 0; st < nstages; ++st) {
     unroll<SPS>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       if (i == SPS - 1) {
         stash_scales(st + 1);   // scales of stage st+1 (ignored past the last stage)
-        stage_barrier<SPS>();
+        // one store per two slices since the last key DMA: SPS/2, or one fewer
+        // in the first stage (no store from a previous stage)
+        if (st == 0) stage_barrier<SPS / 2 - 1>();
+        else stage_barrier<SPS / 2>();
         if (st + 2 < nstages) fetch(st + 2);
         if (st + 3 < nstages) ids(st + 3);
       }
       // previous slice: (st, i-1), or the last slice of stage st-1
       const int pkb = i > 0 ? slice_key(st, i - 1) : slice_key(st - 1, SPS - 1);
       if (i % 2 == 0) {
-        const float part = step(st, ic, acc0, acc1, ks0);
-        finish(part, pkb, ks1, i > 0 || st > 0);
+        hp = step(st, ic, acc0, acc1, ks0);
+        hkb = pkb;
+        hks = ks1;
+        hvalid = i > 0 || st > 0;
       } else {
         const float part = step(st, ic, acc1, acc0, ks1);
-        finish(part, pkb, ks0, true);
+        finish2(hp, hkb, hks, hvalid, part, pkb, ks0);
       }
     });
   }
