@@ -81,8 +81,11 @@ __device__ inline float from_ord(uint32_t o) {
   return __uint_as_float(u);
 }
 
+// Scores enter as read; -0 is folded onto +0 here, the only place where the
+// sign of a zero would matter (bucketing maps both zeros alike).
 __device__ inline unsigned long long composite(float s, int j) {
-  return ((unsigned long long)ord_bits(s) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)j);
+  return ((unsigned long long)ord_bits(canon(s)) << 32) |
+         (unsigned long long)(0xFFFFFFFFu - (uint32_t)j);
 }
 
 __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFFFFFFFFu - (uint32_t)c); }
@@ -244,10 +247,10 @@ struct Row {
       for (int v = 0; v < R / 4; ++v) {
         if (4 * NT * v >= n) break;   // uniform
         const float4 g = group(threadIdx.x + NT * v);
-        x[4 * v] = canon(g.x);
-        x[4 * v + 1] = canon(g.y);
-        x[4 * v + 2] = canon(g.z);
-        x[4 * v + 3] = canon(g.w);
+        x[4 * v] = g.x;
+        x[4 * v + 1] = g.y;
+        x[4 * v + 2] = g.z;
+        x[4 * v + 3] = g.w;
       }
     }
   }
@@ -273,7 +276,7 @@ struct Row {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int j0 = 4 * (v0 + u * NT);
-          const float g[4] = {canon(q[u].x), canon(q[u].y), canon(q[u].z), canon(q[u].w)};
+          const float g[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
           if (j0 < n && (!KEPT || j0 + 4 > lo_)) f(g, j0, GroupRange<KEPT>{lo() - j0, n - j0});
         }
       }
@@ -310,7 +313,7 @@ struct Row {
           const float s[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if ((!KEPT || j0 + e >= lo_) && j0 + e < n) f(canon(s[e]), j0 + e);
+            if ((!KEPT || j0 + e >= lo_) && j0 + e < n) f(s[e], j0 + e);
         }
       }
     }
