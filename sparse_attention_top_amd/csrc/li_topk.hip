@@ -90,6 +90,21 @@ __device__ inline unsigned long long composite(float s, int j) {
 
 __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFFFFFFFFu - (uint32_t)c); }
 
+// The fast path's composite for rows of at most 2^20 keys also carries the
+// key's bucket b in the top 12 bits of its low word: (ord(score), b, 2^20-1-j).
+// Inside a bucket segment the order is the plain composite's (b is common);
+// a key of a lower bucket has a lower score, so its composite is lower whatever
+// its low word holds.
+constexpr uint32_t kIdxMask = (1u << 20) - 1;
+__device__ inline unsigned long long bucket_composite(float s, int b, int j) {
+  return ((unsigned long long)ord_bits(canon(s)) << 32) |
+         (unsigned long long)(((uint32_t)b << 20) | (kIdxMask - (uint32_t)j));
+}
+__device__ inline int bucket_of(unsigned long long c) { return (int)((uint32_t)c >> 20); }
+__device__ inline int32_t bucket_index_of(unsigned long long c) {
+  return (int32_t)(kIdxMask - ((uint32_t)c & kIdxMask));
+}
+
 // Where a record's result goes: output slots idx[d] / val[d] (val may be null).
 // A key's stored index is its position in the record's input, mapped through
 // gather when the input is a split row's candidate lists, plus off.
@@ -98,8 +113,8 @@ struct Out {
   float* val;
   const int32_t* gather;
   int32_t off;
-  __device__ void put(uint32_t d, unsigned long long c) const {
-    const int32_t j = index_of(c);
+  __device__ void put(uint32_t d, unsigned long long c) const { put_key(d, index_of(c), c); }
+  __device__ void put_key(uint32_t d, int32_t j, unsigned long long c) const {
     idx[d] = (gather ? gather[j] : j) + off;
     if (val) val[d] = from_ord((uint32_t)(c >> 32));
   }
@@ -426,7 +441,10 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (rng.ok(e) && b[e] >= t) sm.buf[pos[e]] = composite(x[e], j0 + e);
+      if (rng.ok(e) && b[e] >= t) {
+        if constexpr (W16) sm.buf[pos[e]] = bucket_composite(x[e], b[e], j0 + e);
+        else sm.buf[pos[e]] = composite(x[e], j0 + e);
+      }
   });
   __syncthreads();
   const uint32_t ncand = cnt.get(t);
@@ -450,7 +468,8 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      bk[u] = bucket(from_ord((uint32_t)(me[u] >> 32)));
+      if constexpr (W16) bk[u] = bucket_of(me[u]);
+      else bk[u] = bucket(from_ord((uint32_t)(me[u] >> 32)));
       s0[u] = bk[u] == kBuckets - 1 ? 0u : cnt.get(bk[u] + 1);
       s1[u] = p0 + u * NT < ncand ? cnt.get(bk[u]) : s0[u];
       rank[u] = 0;
@@ -469,7 +488,10 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (s0[u] < s1[u] && !(bk[u] == t && rank[u] >= need)) out.put(s0[u] + rank[u], me[u]);
+      if (s0[u] < s1[u] && !(bk[u] == t && rank[u] >= need)) {
+        if constexpr (W16) out.put_key(s0[u] + rank[u], bucket_index_of(me[u]), me[u]);
+        else out.put(s0[u] + rank[u], me[u]);
+      }
     }
   }
   fill_tail(m, K, out, NT);
