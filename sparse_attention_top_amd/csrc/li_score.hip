@@ -212,7 +212,11 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
   // The query rows sit after both key stages if they fit there, else over the
   // second stage (which is then loaded once they have been read).
   constexpr bool QOVER = 2 * STAGE + WQ * QROW + QEXTRA > LDS_CAP;
-  constexpr int QOFF = QOVER ? STAGE : 2 * STAGE;
+  // Rows too large to sit beside a stage may still fit over both stage buffers:
+  // they are then staged and read before the first key stage is loaded.
+  constexpr bool QALL = !QLDS && !QUANT && ROW >= 256 && WQ * QROW <= 2 * STAGE;
+  constexpr bool QSTAGED = QLDS || QALL;
+  constexpr int QOFF = QALL ? 0 : (QOVER ? STAGE : 2 * STAGE);
   constexpr int KBUF = QLDS ? (QOFF + WQ * QROW > 2 * STAGE ? QOFF + WQ * QROW : 2 * STAGE)
                             : 2 * STAGE;
 
@@ -326,10 +330,10 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
 
   const int nstages = (it.k1 - it.k0 + KT - 1) / KT;
   ids(0);
-  fetch(0);
+  if (!QALL) fetch(0);
   if (!(QLDS && QOVER)) stash_scales(0);
   Frag qf[NT][KSTEPS];
-  if constexpr (QLDS) {
+  if constexpr (QSTAGED) {
     // The row's N1 x ROW query bytes go to LDS as coalesced 1 KB blocks (split
     // over the row's WK waves), head h laid out like key row h, and come back
     // as A-operands with the key fragments' conflict-free reads. Bytes past the
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
     ids(1);
     if (!QOVER) fetch(1);
   }
-  if (!(QLDS && QOVER) && nstages > 2) ids(2);
+  if (!(QLDS && QOVER) && !QALL && nstages > 2) ids(2);
   // The per-lane weights of the 16 heads each lane accumulates per tile.
   float wr[NT][16];
   {
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
         wr[t][e] = (row_ok && he < a.n1) ? wr[t][e] : 0.f;
       }
   }
-  if constexpr (QLDS) {
+  if constexpr (QSTAGED) {
     stage_barrier<0>();   // stage 0 (and 1 if apart from the rows), rows staged, weights in registers
     if (QOVER) stash_scales(0);
 #pragma unroll
@@ -426,7 +430,17 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[t][s] = read_frag(qb, s) & mask;
     }
-    if constexpr (QOVER) {
+    if constexpr (QALL) {
+      stage_barrier<0>();   // query rows read: both stage buffers are free
+      fetch(0);
+      if (nstages > 1) {
+        ids(1);
+        fetch(1);
+      }
+      if (nstages > 2) ids(2);
+      if (nstages > 1) stage_barrier<DPW>();   // stage 0 staged (stage 1 may still load)
+      else stage_barrier<0>();
+    } else if constexpr (QOVER) {
       stage_barrier<0>();   // query rows read (their space takes stage 1), scales published
       if (nstages > 1) fetch(1);
       if (nstages > 2) ids(2);
