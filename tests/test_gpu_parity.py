@@ -199,6 +199,13 @@ EDGE = {
                                  w_dtype="f16", N1=37, D=128, seqlens_q=[2, 1, 2],
                                  seqlens_k=[3000, 64, 5000], block_size=128, sparse_count=256,
                                  sparse_mode=3),
+    # prefill tiles whose rows are staged over both key buffers before the first
+    # key stage loads, with paged keys in 16-key blocks: one, one and three
+    # 256-key stages per tile
+    "lds_query_prefill_paged_stages": dict(layout_q="BSND", layout_k="PA_BSND",
+                                           qk_dtype="bf16", w_dtype="bf16", N1=64, D=128,
+                                           seqlens_q=[8, 6, 9], seqlens_k=[200, 9, 600],
+                                           block_size=16, sparse_count=64, sparse_mode=3),
 }
 
 
