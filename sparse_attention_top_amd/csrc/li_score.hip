@@ -420,7 +420,9 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
       }
   }
   if constexpr (QSTAGED) {
-    stage_barrier<0>();   // stage 0 (and 1 if apart from the rows), rows staged, weights in registers
+    // rows staged, weights in registers, and (unless the rows fill both stage
+    // buffers) stage 0, and stage 1 if apart from the rows
+    stage_barrier<0>();
     if (QOVER) stash_scales(0);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
