@@ -175,7 +175,9 @@ typedef struct li_problem {
  *                rejected for BSND and PA_BSND.
  *  seqused_q     (B) int32, optional: actual query length of each batch, <= s1
  *                (BSND) or <= the cu_seqlens_q length (TND); rows past it are
- *                unused. NULL means the full length.
+ *                unused (all -1 / -inf; under TND this is the V2 guide's "TND
+ *                Padding" of its constraint list), and the causal rule takes
+ *                it as S_q. NULL means the full length.
  *  seqused_k     (B) int32: actual key lengths. Optional for BSND (<= s2) and
  *                TND (<= the cu_seqlens_k length), NULL meaning the full length;
  *                required for PA_BSND (covered by max_blocks_per_seq blocks).
@@ -237,32 +239,63 @@ li_status li_metadata(const li_problem* p, const li_lengths* lengths, int32_t nu
  * li_workspace_size -- host-only: bytes of device workspace li_score/li_indexer
  * need: the head-reduced float32 scores of every visible (row, key) pair and,
  * when the task table splits long rows (few rows, k <= 2048), the candidate
- * lists that li_topk passes between its two passes.
+ * lists that li_topk passes between its two passes. This is the first half of
+ * the two-stage pattern the V2 guide describes for the aclnn interface
+ * ("与其他调用方式的关系": a GetWorkspaceSize call, then the launch with the
+ * caller's workspace).
+ *  meta_host     the table li_metadata wrote for this same problem.
+ *  bytes         out: workspace bytes (at least 4).
+ * Errors: LI_ERR_METADATA_MISMATCH if the table was built for another problem
+ * (any field hashed into it, sparse_count, init_num and local_num included).
  */
 li_status li_workspace_size(const li_problem* p, const void* meta_host, size_t* bytes);
 
 /*
  * li_score -- enqueue the score kernel: s_j for every visible (row, key) pair,
- * written as float32 into the workspace (layout private to the library).
- *  meta_host / meta_dev  the same table, on the host and on the device.
- *  ws, ws_bytes  device workspace of at least li_workspace_size() bytes.
+ * written as float32 into the workspace (layout private to the library). The
+ * score is the MindSpore page's formula block (the sum over heads of
+ * W * ReLU(q . k)), the quantised README's function-description formula for
+ * E4M3FN / I8, with the V2 guide's visibility rules (sparse_mode, actual
+ * lengths, cmp_ratio).
+ *  in            device operands (see li_inputs).
+ *  meta_host / meta_dev  the same table, on the host and on the device
+ *                (16-byte aligned); only meta_host is read by the call.
+ *  ws, ws_bytes  device workspace of at least li_workspace_size() bytes,
+ *                16-byte aligned; q and k must be 16-byte aligned too.
  *  stream        hipStream_t (NULL = default stream).
+ * Errors (nothing enqueued): LI_ERR_INVALID_ARGUMENT for a missing operand or
+ * a misaligned pointer, LI_ERR_METADATA_MISMATCH, LI_ERR_WORKSPACE_TOO_SMALL,
+ * LI_ERR_HIP if the launch fails.
  */
 li_status li_score(const li_problem* p, const li_inputs* in, const void* meta_host,
                    const void* meta_dev, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * li_topk -- enqueue the per-row top-k over a workspace filled by li_score.
+ * li_topk -- enqueue the per-row top-k over a workspace filled by li_score:
+ * the k largest scores of each row, sorted by descending score, equal scores
+ * by ascending key index (the V2 guide asks for a deterministic result,
+ * "确定性计算"; the TileLang guide's golden takes the largest k, sorted), the
+ * unused slots holding -1 / -inf (V2 guide, constraint list).
+ *  meta_host / meta_dev  as for li_score.
  *  ws, ws_bytes    the workspace li_score filled; the scores are only read, the
  *                  candidate-list part (split rows) is written.
  *  sparse_indices  device int32, (B,S1,N2,k) or (T1,N2,k).
  *  sparse_values   device float32 of the same shape; required iff return_value.
+ * Errors (nothing enqueued): LI_ERR_INVALID_ARGUMENT (missing output, values
+ * requested without a buffer, misaligned workspace), LI_ERR_METADATA_MISMATCH,
+ * LI_ERR_WORKSPACE_TOO_SMALL, LI_ERR_HIP.
  */
 li_status li_topk(const li_problem* p, const void* meta_host, const void* meta_dev,
                   void* ws, size_t ws_bytes, int32_t* sparse_indices,
                   float* sparse_values, void* stream);
 
-/* li_indexer -- li_score followed by li_topk on the same stream. */
+/*
+ * li_indexer -- li_score followed by li_topk on the same stream: the whole
+ * operator of the MindSpore page's signature (query, key, weights, lengths,
+ * block table, sparse_count, sparse_mode, return_value) with the workspace and
+ * task table of the V2 guide's two-call protocol. Both halves are validated
+ * before either is enqueued; arguments and errors as for li_score and li_topk.
+ */
 li_status li_indexer(const li_problem* p, const li_inputs* in, const void* meta_host,
                      const void* meta_dev, void* ws, size_t ws_bytes,
                      int32_t* sparse_indices, float* sparse_values, void* stream);

@@ -22,7 +22,11 @@ per head, ReLU, multiply by the per-head weight, sum over the heads, top-k
 with largest first and sorted output):
 
 1. actual lengths per batch: S_q, S_k (BSND: seqused or the padded dim;
-   TND: cu_seqlens differences; PA_BSND: seqused_k);
+   TND: seqused where given, else the cu_seqlens differences; PA_BSND:
+   seqused_k). Under TND a seqused_q below the cu_seqlens_q length is the
+   LightningIndexerV2 guide's "TND Padding" (constraint list, Ascend 950
+   items): the query rows between the two lengths are allotted in the output
+   but invalid, so they come out all -1 / -inf like any row past S_q;
 2. visible keys of query row i: all S_k for sparse_mode 0; for sparse_mode 3
    (right-down causal) key j is visible iff j <= i + S_k - S_q, i.e. the
    first clamp(i + 1 + S_k - S_q, 0, S_k) keys;
@@ -146,19 +150,24 @@ def decode(arr: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def batch_lengths(wl) -> List[Tuple[int, int]]:
-    """Actual (S_q, S_k) per batch, from the length inputs the pages define."""
+    """Actual (S_q, S_k) per batch, from the length inputs the pages define.
+
+    seqused_* wins over the allotted length in every layout: the padded dim for
+    BSND, the cu_seqlens difference for TND (the V2 guide's TND padding rule
+    for queries; seqused_k is optional for BSND and TND keys, required for
+    PA_BSND, in the same guide's constraint list)."""
     out = []
     for b in range(wl.B):
-        if wl.layout_q == "TND":
-            sq = int(wl.cu_seqlens_q[b + 1]) - int(wl.cu_seqlens_q[b])
-        elif wl.seqused_q is not None:
+        if wl.seqused_q is not None:
             sq = int(wl.seqused_q[b])
+        elif wl.layout_q == "TND":
+            sq = int(wl.cu_seqlens_q[b + 1]) - int(wl.cu_seqlens_q[b])
         else:
             sq = int(wl.q.shape[1])
-        if wl.layout_k == "TND":
-            sk = int(wl.cu_seqlens_k[b + 1]) - int(wl.cu_seqlens_k[b])
-        elif wl.seqused_k is not None:
+        if wl.seqused_k is not None:
             sk = int(wl.seqused_k[b])
+        elif wl.layout_k == "TND":
+            sk = int(wl.cu_seqlens_k[b + 1]) - int(wl.cu_seqlens_k[b])
         else:
             sk = int(wl.k.shape[1])
         out.append((sq, sk))
@@ -307,7 +316,9 @@ def select_blocks(sb: np.ndarray, k: int, init_num: int, local_num: int) -> Tupl
 
 
 def all_rows(wl) -> List[Tuple[int, int]]:
-    """Every output row as (batch, position)."""
+    """Every output row as (batch, position): the rows allotted to each
+    sequence (S1 for BSND, the cu_seqlens_q difference for TND), padding rows
+    included."""
     rows = []
     for b in range(wl.B):
         n = (int(wl.cu_seqlens_q[b + 1]) - int(wl.cu_seqlens_q[b])

@@ -246,7 +246,7 @@ META_HEADER_DTYPE = np.dtype([
     ("off_batches", "<u8"), ("off_items", "<u8"), ("max_sk", "<i4"), ("max_sq", "<i4"),
     ("off_rows", "<u8"), ("row_class", "<i4", (2 * TOPK_CLASSES + 1,)), ("split_rows", "<i4"),
     ("cand_val_off", "<i8"), ("cand_idx_off", "<i8"), ("num_recs", "<i8"),
-    ("reserved", "<i4", (4,)),
+    ("sparse_count", "<i4"), ("init_num", "<i4"), ("local_num", "<i4"), ("reserved", "<i4"),
 ])
 assert META_HEADER_DTYPE.itemsize == 176
 BATCH_REC_DTYPE = np.dtype([("ws_off", "<i8"), ("row_base", "<i4"), ("k_base", "<i4"),

@@ -134,10 +134,13 @@ int32_t cmp_ratio_of(const li_problem& p) { return p.cmp_ratio > 1 ? p.cmp_ratio
 int32_t block_len_of(const li_problem& p) { return p.block_len > 1 ? p.block_len : 1; }
 
 uint64_t problem_hash(const li_problem& p) {
-  // FNV-1a over the fields that shape the work decomposition.
+  // FNV-1a over every field that shapes the task table: the work items, the
+  // workspace layout, the top-k records (output offsets row * k, the split of
+  // long rows, candidate-list sizes) and the kept-block selection.
   const int64_t f[] = {p.layout_q, p.layout_k, p.dtype_qk, p.batch, p.s1, p.s2, p.n1, p.n2, p.d,
                        p.t1, p.t2, p.block_size, p.max_blocks_per_seq, p.num_blocks,
-                       p.sparse_mode, cmp_ratio_of(p), block_len_of(p)};
+                       p.sparse_mode, cmp_ratio_of(p), block_len_of(p), p.sparse_count,
+                       p.init_num, p.local_num};
   uint64_t h = 1469598103934665603ull;
   const unsigned char* b = reinterpret_cast<const unsigned char*>(f);
   for (size_t i = 0; i < sizeof f; ++i) {
@@ -159,6 +162,13 @@ li_status check_meta(const li_problem& p, const void* meta_host, const MetaHeade
   LI_CHECK(h->problem_hash == problem_hash(p) && h->batch == p.batch &&
                h->num_rows == num_rows(p),
            LI_ERR_METADATA_MISMATCH, "task table was built for another problem");
+  // The fields the row records depend on are also compared one by one, so that
+  // a hash collision cannot let a table of another k through.
+  LI_CHECK(h->sparse_count == p.sparse_count && h->init_num == p.init_num &&
+               h->local_num == p.local_num,
+           LI_ERR_METADATA_MISMATCH,
+           "task table was built for sparse_count %d, init_num %d, local_num %d (problem: %d, %d, %d)",
+           h->sparse_count, h->init_num, h->local_num, p.sparse_count, p.init_num, p.local_num);
   *out = h;
   return LI_OK;
 }
@@ -477,6 +487,9 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
     h.cand_val_off = cand > 0 ? cand_val_off : 0;
     h.cand_idx_off = cand > 0 ? cand_idx_off : 0;
     h.num_recs = nrecs;
+    h.sparse_count = p->sparse_count;
+    h.init_num = p->init_num;
+    h.local_num = p->local_num;
     uint8_t* dst = static_cast<uint8_t*>(meta_host);
     std::memcpy(dst + off_b, recs.data(), sizeof(BatchRec) * (size_t)B);
     WorkItem* items = reinterpret_cast<WorkItem*>(dst + off_i);

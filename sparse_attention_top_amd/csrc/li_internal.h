@@ -29,7 +29,7 @@ namespace li {
 // a second-pass record selects the row's top k among the chunk lists.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMetaMagic = 0x444D494Cu;  // "LIMD"
-constexpr uint32_t kMetaVersion = 6;
+constexpr uint32_t kMetaVersion = 7;
 
 // Top-k size classes: class c holds the rows of at most kTopkClassKeys[c]
 // visible keys (the last class is unbounded) and runs with kTopkClassThreads[c]
@@ -75,7 +75,12 @@ struct MetaHeader {
   int64_t cand_val_off;    // workspace float offset of the candidate values
   int64_t cand_idx_off;    // ... of the candidate indices (int32 in float slots)
   int64_t num_recs;        // RowRec records of both passes
-  int32_t reserved[4];
+  // Selection fields the row records are laid out for (output offsets row*k,
+  // the split decision, candidate-list sizes); also covered by problem_hash.
+  int32_t sparse_count;
+  int32_t init_num;
+  int32_t local_num;
+  int32_t reserved;
 };
 static_assert(sizeof(MetaHeader) == 176, "header size");
 
@@ -86,7 +91,7 @@ struct BatchRec {
   int32_t s_q;      // actual query length
   int32_t s_k;      // actual key length (compressed keys when cmp_ratio > 1)
   int32_t ld;       // workspace row stride in floats (multiple of 4)
-  int32_t rows;     // output rows allotted to the sequence (S1 for BSND, s_q for TND)
+  int32_t rows;     // output rows allotted to the sequence (S1 for BSND, the cu_seqlens_q length for TND)
   int32_t cmp_res;  // original tokens past the last whole compressed key (0 if none)
   int32_t reserved;
 };

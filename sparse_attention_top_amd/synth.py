@@ -25,9 +25,9 @@ e4m3fn      uint8                OCP FP8 E4M3FN codes
 i8          int8                 signed 8-bit integer codes
 ==========  ===================  =============================
 
-Padding that must never be read (BSND keys past ``seqused_k``, the tail rows
-of a partly used paged block, unused physical blocks) is filled with a poison
-value of +30 so any out-of-length read shows up as a dominant score.
+Padding that must never be read (BSND and TND keys past ``seqused_k``, the
+tail rows of a partly used paged block, unused physical blocks) is filled with
+a poison value of +30 so any out-of-length read shows up as a dominant score.
 """
 from __future__ import annotations
 
@@ -211,25 +211,43 @@ def build(name: str, *, layout_q: str, layout_k: str, qk_dtype: str, w_dtype: st
           pass_seqused_k: Optional[bool] = None,
           cmp_ratio: int = 1, cmp_residual_k: Optional[Sequence[int]] = None,
           output_idx_offset: Optional[Sequence[int]] = None, block_len: int = 1,
-          init_num: int = 0, local_num: int = 0) -> Workload:
-    """Draw one problem. Draw order: q, k, w, then the paged block permutation."""
+          init_num: int = 0, local_num: int = 0,
+          padded_q: Optional[Sequence[int]] = None,
+          padded_k: Optional[Sequence[int]] = None) -> Workload:
+    """Draw one problem. Draw order: q, k, w, then the paged block permutation.
+
+    seqlens_q / seqlens_k are the actual lengths. padded_q / padded_k (TND
+    only) are the rows each sequence is allotted in the packed tensor (the
+    cu_seqlens differences, each >= the actual length); the actual lengths are
+    then passed as seqused_q / seqused_k (the V2 guide's TND padding), query
+    rows in between are padding rows and keys in between are poisoned."""
     if layout_k != "PA_BSND" and layout_k != layout_q:
         raise ValueError("non-paged key layout must equal the query layout")
     sl_q = np.asarray(seqlens_q, dtype=np.int32)
     sl_k = np.asarray(seqlens_k, dtype=np.int32)
     B = int(sl_q.shape[0])
     assert sl_k.shape == (B,)
+    if padded_q is not None:
+        assert layout_q == "TND"
+        pad_q = np.asarray(padded_q, dtype=np.int32)
+        assert pad_q.shape == (B,) and (pad_q >= sl_q).all()
+    if padded_k is not None:
+        assert layout_k == "TND"
+        pad_k = np.asarray(padded_k, dtype=np.int32)
+        assert pad_k.shape == (B,) and (pad_k >= sl_k).all()
     dr = _Draw(seed)
     wl_kw = {}
 
     # ---------------- query ----------------
     if layout_q == "TND":
         cu_q = np.zeros(B + 1, np.int32)
-        cu_q[1:] = np.cumsum(sl_q)
+        cu_q[1:] = np.cumsum(sl_q if padded_q is None else pad_q)
         T1 = int(cu_q[-1])
         qf = dr.normal((T1, N1, D))
         S1v = int(sl_q.max()) if B else 0
         wl_kw["cu_seqlens_q"] = cu_q
+        if padded_q is not None:
+            wl_kw["seqused_q"] = sl_q.copy()
     else:
         S1v = int(S1) if S1 is not None else int(sl_q.max())
         assert (sl_q <= S1v).all()
@@ -245,10 +263,14 @@ def build(name: str, *, layout_q: str, layout_k: str, qk_dtype: str, w_dtype: st
     # ---------------- key ----------------
     if layout_k == "TND":
         cu_k = np.zeros(B + 1, np.int32)
-        cu_k[1:] = np.cumsum(sl_k)
+        cu_k[1:] = np.cumsum(sl_k if padded_k is None else pad_k)
         kf = dr.normal((int(cu_k[-1]), N2, D))
         S2v = int(sl_k.max()) if B else 0
         wl_kw["cu_seqlens_k"] = cu_k
+        if padded_k is not None:
+            for b in range(B):                   # never-read padding
+                kf[int(cu_k[b]) + int(sl_k[b]):int(cu_k[b + 1])] = POISON
+            wl_kw["seqused_k"] = sl_k.copy()
         k, k_scale = _encode_qk(kf, qk_dtype)
     elif layout_k == "BSND":
         S2v = int(S2) if S2 is not None else int(sl_k.max())

@@ -45,15 +45,23 @@ def visible_pairs(wl) -> int:
 
 
 class RowStats:
+    """Counts over the checked rows, plus two guards on the band floor:
+    max_err_m, the largest |v_j - s_j| / M over every returned value (M = the
+    row's largest score magnitude), and floor_rows, the rows that would fail
+    one of rules 2-5 if the floor 2^-6 M were dropped (tau = tol * |s_(k)|)."""
+
     def __init__(self):
         self.rows = 0
         self.exact_set = 0
         self.in_band = 0
         self.all_keys = 0
+        self.max_err_m = 0.0
+        self.floor_rows = 0
 
     def __repr__(self):
         return (f"rows={self.rows} exact_set={self.exact_set} tie_band={self.in_band} "
-                f"all_keys={self.all_keys}")
+                f"all_keys={self.all_keys} max_err/M={self.max_err_m:.3g} "
+                f"floor_rows={self.floor_rows}")
 
 
 def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: int,
@@ -77,6 +85,7 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
     srt = np.sort(s)[::-1]
     s1 = np.abs(s).max()
     floor = 2.0 ** -6 * s1
+    needs_floor = False
     if n <= k:
         assert np.array_equal(np.sort(head), np.arange(n)), f"{where}: must return every key"
         tau = tol * max(abs(srt[-1]), floor)
@@ -92,6 +101,9 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
         must = np.nonzero(s > sk + tau)[0]
         missing = np.setdiff1d(must, head)
         assert missing.size == 0, f"{where}: missing clear winners {missing[:5]}"
+        tau0 = tol * abs(sk)
+        needs_floor |= bool((sel < sk - tau0).any())
+        needs_floor |= np.setdiff1d(np.nonzero(s > sk + tau0)[0], head).size > 0
         if stats is not None:
             if oidx is not None and np.array_equal(np.sort(head), np.sort(oidx[:m])):
                 stats.exact_set += 1
@@ -110,6 +122,11 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
         assert (err <= lim).all(), f"{where}: values off by up to {err.max():.3g} " \
                                    f"(limit {lim[np.argmax(err - lim)]:.3g})"
         assert (np.diff(v) <= 0).all(), f"{where}: values not non-increasing"
+        needs_floor |= bool((err > tol * np.abs(sh)).any())
+        if stats is not None and s1 > 0:
+            stats.max_err_m = max(stats.max_err_m, float(err.max() / s1))
+    if stats is not None and needs_floor:
+        stats.floor_rows += 1
 
 
 def check_rows(gidx_rows: np.ndarray, gval_rows: Optional[np.ndarray], oracle_out: dict,

@@ -235,6 +235,18 @@ WORKLOADS = {
                                           seqlens_q=[128, 1, 50], seqlens_k=[1000, 9, 13],
                                           sparse_count=16, sparse_mode=3, cmp_ratio=128,
                                           cmp_residual_k=[127, 5, 0], seed=8),
+    # TND padding: seqused_q / seqused_k below the cu_seqlens lengths, one
+    # sequence with no used query rows
+    "tnd_padding": lambda: synth.build("tp", layout_q="TND", layout_k="TND", qk_dtype="bf16",
+                                       w_dtype="bf16", N1=16, D=64, seqlens_q=[30, 0, 9, 4],
+                                       seqlens_k=[90, 12, 9, 0], padded_q=[41, 5, 9, 6],
+                                       padded_k=[100, 12, 20, 3], sparse_count=16,
+                                       sparse_mode=3, seed=11),
+    "tnd_padding_paged": lambda: synth.build("tpp", layout_q="TND", layout_k="PA_BSND",
+                                             qk_dtype="e4m3fn", w_dtype="f32", N1=8, D=128,
+                                             seqlens_q=[3, 0, 7], seqlens_k=[300, 40, 129],
+                                             padded_q=[5, 2, 7], block_size=64,
+                                             sparse_count=32, sparse_mode=3, seed=12),
     "compressed_nomask": lambda: synth.build("zn", layout_q="BSND", layout_k="BSND",
                                              qk_dtype="bf16", w_dtype="bf16", N1=8, D=64,
                                              seqlens_q=[9, 9], seqlens_k=[40, 40],
@@ -397,16 +409,66 @@ def test_metadata_heaviest_first_and_balanced(lib):
     assert int(h["num_items"]) >= 4 * 256
 
 
-def test_metadata_mismatch_rejected(lib):
+MISMATCH = [
+    ("s2", dict(s2=65)),
+    ("k 8", dict(sparse_count=8)),        # row records would write row*2048 into rows*8
+    ("k 4096", dict(sparse_count=4096)),  # ... or overrun the candidate lists
+    ("k 2047", dict(sparse_count=2047)),
+    ("init_num", dict(init_num=2)),       # kept blocks change the split decision
+    ("local_num", dict(local_num=3)),
+    ("block_len", dict(block_len=4)),
+    ("cmp_ratio", dict(cmp_ratio=4, sparse_mode=0)),
+    ("sparse_mode", dict(sparse_mode=0)),
+    ("dtype", dict(dtype_qk="f16")),
+]
+
+
+@pytest.mark.parametrize("name,kw", MISMATCH, ids=[m[0] for m in MISMATCH])
+def test_metadata_mismatch_rejected(lib, name, kw):
+    """A table built for one problem (k = 2048, a few long rows that split) is
+    rejected for another by every call that takes it, before any launch."""
+    base = dict(layout_q="TND", layout_k="TND", t1=2, t2=30000, batch=1, n1=8, d=64,
+                sparse_count=2048, sparse_mode=3)
+    p = _prob(**base)
+    L = B.make_lengths(cu_seqlens_q=[0, 2], cu_seqlens_k=[0, 30000])
+    meta = B.li_metadata(p, L)
+    assert int(B.parse_metadata(meta)[0]["split_rows"]) == 2
+    ws = B.li_workspace_size(p, meta)
+    q = _prob(**{**base, **kw})
+    fake = 1 << 20   # never dereferenced: validation fails first
+    inp = B.make_inputs(fake, fake, fake)
+    calls = {
+        "li_workspace_size": lambda: B.li_workspace_size(q, meta),
+        "li_score": lambda: B.li_score(q, inp, meta, fake, fake, ws),
+        "li_topk": lambda: B.li_topk(q, meta, fake, fake, ws, fake, 0),
+        "li_indexer": lambda: B.li_indexer(q, inp, meta, fake, fake, ws, fake, 0),
+    }
+    for call, f in calls.items():
+        with pytest.raises(B.LIError) as e:
+            f()
+        assert e.value.status == B.ERR_METADATA_MISMATCH, call
+
+
+def test_metadata_junk_rejected(lib):
     p = _prob()
     meta = B.li_metadata(p, B.make_lengths())
-    q = _prob(s2=65)
-    with pytest.raises(B.LIError) as e:
-        B.li_workspace_size(q, meta)
-    assert e.value.status == B.ERR_METADATA_MISMATCH
     junk = np.zeros_like(meta)
     with pytest.raises(B.LIError) as e:
         B.li_workspace_size(p, junk)
+    assert e.value.status == B.ERR_METADATA_MISMATCH
+    h = B.parse_metadata(meta)[0]
+    assert int(h["sparse_count"]) == 32 and int(h["init_num"]) == 0 and int(h["local_num"]) == 0
+
+
+def test_metadata_header_fields_checked_apart_from_hash(lib):
+    """The k the row records are laid out for is compared on its own too: a
+    table whose stored k was altered (hash intact) is rejected."""
+    p = _prob()
+    meta = B.li_metadata(p, B.make_lengths()).copy()
+    hdr = meta[:B.META_HEADER_DTYPE.itemsize].view(B.META_HEADER_DTYPE)
+    hdr["sparse_count"] = 31
+    with pytest.raises(B.LIError) as e:
+        B.li_workspace_size(p, meta)
     assert e.value.status == B.ERR_METADATA_MISMATCH
 
 

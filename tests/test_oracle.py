@@ -181,6 +181,9 @@ def _hand_workload(case):
         ns.layout_q = ns.layout_k = "TND"
         ns.cu_seqlens_q = np.array(case["cu_seqlens_q"], np.int32)
         ns.cu_seqlens_k = np.array(case["cu_seqlens_k"], np.int32)
+        for f in ("seqused_q", "seqused_k"):   # TND padding
+            if f in case:
+                setattr(ns, f, np.array(case[f], np.int32))
         ns.q = _enc(qv, dt)
         ns.w = wv
         ns.k = _enc(np.array(case["keys"])[:, None, :], dt)
@@ -513,3 +516,40 @@ def test_poisoned_padding_never_selected():
     wl = _small(28, seqlens_q=[40], seqlens_k=[50], S2=70, sparse_mode=0)
     o = O.run(wl)
     assert o["indices"].max() < 50
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_tnd_padding_equals_unpadded(mode):
+    """TND padding (V2 guide, constraint list): rows past seqused_q inside a
+    sequence's cu_seqlens_q range come out all -1 / -inf, and the used rows
+    equal the same problem packed without the padding (the causal rule takes
+    the used lengths). Keys past seqused_k hold the +30 poison and are never
+    chosen."""
+    kw = dict(layout_q="TND", layout_k="TND", qk_dtype="bf16", w_dtype="f32", N1=8, D=32,
+              seqlens_q=[12, 0, 7], seqlens_k=[30, 9, 7], sparse_count=6, sparse_mode=mode,
+              seed=29)
+    pad = synth.build("pad", padded_q=[20, 3, 7], padded_k=[40, 9, 11], **kw)
+    o = O.run(pad)
+    rows = 0
+    for b in range(pad.B):
+        q0 = int(pad.cu_seqlens_q[b])
+        used, allotted = int(pad.seqused_q[b]), int(pad.cu_seqlens_q[b + 1]) - q0
+        k0, sk = int(pad.cu_seqlens_k[b]), int(pad.seqused_k[b])
+        assert (o["indices"][q0 + used:q0 + allotted] == -1).all()
+        assert np.isneginf(o["values"][q0 + used:q0 + allotted]).all()
+        if used == 0:
+            continue
+        one = SimpleNamespace(B=1, layout_q="TND", layout_k="TND", qk_dtype="bf16",
+                              w_dtype="f32", N1=8, N2=1, D=32, sparse_count=6, sparse_mode=mode,
+                              q=pad.q[q0:q0 + used], k=pad.k[k0:k0 + sk],
+                              w=pad.w[q0:q0 + used], q_scale=None, k_scale=None,
+                              cu_seqlens_q=np.array([0, used], np.int32),
+                              cu_seqlens_k=np.array([0, sk], np.int32), seqused_q=None,
+                              seqused_k=None, block_table=None)
+        ob = O.run(one)
+        assert np.array_equal(o["indices"][q0:q0 + used], ob["indices"])
+        assert np.array_equal(o["values"][q0:q0 + used], ob["values"])
+        assert o["indices"][q0:q0 + used].max() < sk
+        rows += used
+    assert rows == 19
+    _check_structure(pad, o)
