@@ -279,6 +279,24 @@ def row_scores(q: np.ndarray, w: np.ndarray, k: np.ndarray,
     return w @ np.maximum(x, 0.0)
 
 
+def row_magnitudes(q: np.ndarray, w: np.ndarray, k: np.ndarray,
+                   q_scale: Optional[np.ndarray] = None,
+                   k_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """P_j = sum_g |w[g]| * |q_scale[g] * k_scale[j]| * sum_d |q[g, d] * k[j, d]|.
+
+    Not part of the method: the sum of the magnitudes of every product that
+    enters s_j (same arguments as row_scores). Any floating-point evaluation
+    of s_j (dot products over D, the head sum over G, the scale products) has
+    a forward error of at most a small multiple of (D + G) * unit roundoff *
+    P_j, whatever the summation order (the standard error bound for inner
+    products and sums), which is how the tests judge how far a float32 result
+    may lie from the exact score when the terms cancel."""
+    x = np.abs(q) @ np.abs(k).T
+    if q_scale is not None:
+        x = (np.abs(q_scale)[:, None] * np.abs(k_scale)[None, :]) * x
+    return np.abs(w) @ x
+
+
 def topk_order(s: np.ndarray, k: int) -> np.ndarray:
     """Positions of the k largest entries of s, by (score desc, index asc)."""
     n = s.shape[0]
@@ -338,6 +356,9 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
       'scores'  : (if want_scores) list over rows of lists over N2 of float64
                   arrays holding s_j for every visible key j (block scores
                   for block_len > 1);
+      'mags'    : (if want_scores) the same layout as 'scores', holding
+                  row_magnitudes of each key (for blocks: the largest over
+                  the block's visible keys);
       'kept'    : (if want_scores) int (R, N2): output slots taken by the
                   blocks that are always kept (0 without init_num / local_num).
     """
@@ -348,6 +369,7 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
     idx = np.full((R, N2, kk), -1, np.int32)
     val = np.full((R, N2, kk), -np.inf, np.float32)
     scores: List[List[np.ndarray]] = [[np.zeros(0)] * N2 for _ in range(R)]
+    mags: List[List[np.ndarray]] = [[np.zeros(0)] * N2 for _ in range(R)]
     kept = np.zeros((R, N2), np.int64)
     lengths = batch_lengths(wl)
     L, init_num, local_num = routing(wl)
@@ -385,9 +407,14 @@ def run(wl, rows: Optional[Iterable[Tuple[int, int]]] = None, want_scores: bool 
                     val[r, h, :m] = s[order].astype(np.float32)
                     if want_scores:
                         scores[r][h] = s
+                        p = row_magnitudes(q[t, g], w[t, g], keys[:n, h],
+                                           None if qs is None else qs[t, g],
+                                           None if kscale is None else kscale[:n, h])
+                        mags[r][h] = block_scores(p, L) if L > 1 else p
     out: Dict[str, object] = {"rows": rows, "indices": idx, "values": val}
     if want_scores:
         out["scores"] = scores
+        out["mags"] = mags
         out["kept"] = kept
     return out
 

@@ -17,6 +17,13 @@ largest score is 0, and only M gives the scale). The GPU row G is accepted iff
 Rules 2-3 make G equal the oracle's set whenever s_(k) and s_(k+1) are more
 than tau apart; inside that band any choice whose oracle score is within tau
 of the k-th is accepted. Rows that see at most k keys must return all of them.
+
+Beside the tolerance, when the oracle's per-key magnitudes P_j (the sum of the
+absolute values of the products in s_j) and an error budget c are given, every
+returned value must also satisfy |v_j - s_j| <= c * 2^-24 * P_j: the forward
+error bound of float32 dot products and sums, whatever their order. A GPU whose
+values meet it computes the formula to float32 accuracy, so neither the
+tolerance nor its floor is doing the work for the values.
 """
 from __future__ import annotations
 
@@ -44,29 +51,43 @@ def visible_pairs(wl) -> int:
     return tot
 
 
+U32 = 2.0 ** -24   # float32 unit roundoff
+
+
+def err_budget(wl) -> float:
+    """Error budget c (in units of 2^-24 * P_j) of a float32 evaluation of the
+    formula: D-term dot products, an N1-term head sum and a few scale and
+    output roundings, doubled to cover any rounding mode of the accumulators."""
+    return 2.0 * (wl.D + wl.N1 // wl.N2 + 4)
+
+
 class RowStats:
     """Counts over the checked rows, plus two guards on the band floor:
-    max_err_m, the largest |v_j - s_j| / M over every returned value (M = the
-    row's largest score magnitude), and floor_rows, the rows that would fail
-    one of rules 2-5 if the floor 2^-6 M were dropped (tau = tol * |s_(k)|)."""
+    max_err_u, the largest |v_j - s_j| / (2^-24 P_j) over every returned value
+    (bounded by the error budget when one is given), max_err_m, the same error
+    over the row's largest score magnitude M, and floor_rows, the rows that
+    would fail one of rules 2-5 if the floor 2^-6 M were dropped
+    (tau = tol * |s_(k)|)."""
 
     def __init__(self):
         self.rows = 0
         self.exact_set = 0
         self.in_band = 0
         self.all_keys = 0
+        self.max_err_u = 0.0
         self.max_err_m = 0.0
         self.floor_rows = 0
 
     def __repr__(self):
         return (f"rows={self.rows} exact_set={self.exact_set} tie_band={self.in_band} "
-                f"all_keys={self.all_keys} max_err/M={self.max_err_m:.3g} "
-                f"floor_rows={self.floor_rows}")
+                f"all_keys={self.all_keys} max_err/(u*P)={self.max_err_u:.3g} "
+                f"max_err/M={self.max_err_m:.3g} floor_rows={self.floor_rows}")
 
 
 def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: int,
               tol: float, oidx: Optional[np.ndarray] = None,
-              stats: Optional[RowStats] = None, where: str = "") -> None:
+              stats: Optional[RowStats] = None, where: str = "",
+              mag: Optional[np.ndarray] = None, budget: Optional[float] = None) -> None:
     n = s.shape[0]
     m = min(k, n)
     gidx = np.asarray(gidx).astype(np.int64)
@@ -123,6 +144,16 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
                                    f"(limit {lim[np.argmax(err - lim)]:.3g})"
         assert (np.diff(v) <= 0).all(), f"{where}: values not non-increasing"
         needs_floor |= bool((err > tol * np.abs(sh)).any())
+        if mag is not None:
+            pm = np.asarray(mag, np.float64)[head]
+            eu = np.where(pm > 0, err / (U32 * np.where(pm > 0, pm, 1.0)),
+                          np.where(err > 0, np.inf, 0.0))
+            if budget is not None:
+                bad = eu > budget
+                assert not bad.any(), f"{where}: values off by {eu.max():.3g} * 2^-24 P_j " \
+                                      f"(budget {budget}) at keys {head[bad][:5]}"
+            if stats is not None:
+                stats.max_err_u = max(stats.max_err_u, float(eu.max()))
         if stats is not None and s1 > 0:
             stats.max_err_m = max(stats.max_err_m, float(err.max() / s1))
     if stats is not None and needs_floor:
@@ -130,12 +161,14 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
 
 
 def check_rows(gidx_rows: np.ndarray, gval_rows: Optional[np.ndarray], oracle_out: dict,
-               k: int, tol: float, label: str = "", offsets=None) -> RowStats:
+               k: int, tol: float, label: str = "", offsets=None,
+               budget: Optional[float] = None) -> RowStats:
     """gidx_rows / gval_rows: (R, N2, k) arrays aligned with oracle_out['rows'].
 
     offsets: per-batch output_idx_offset (or None); returned indices must be the
     key index plus the offset, -1 slots stay -1, and the rule is then applied to
-    the key indices."""
+    the key indices. budget: the float32 error budget (err_budget) the values
+    are held to against the oracle's magnitudes, when it returned them."""
     st = RowStats()
     for r, (b, i) in enumerate(oracle_out["rows"]):
         for h in range(gidx_rows.shape[1]):
@@ -150,17 +183,19 @@ def check_rows(gidx_rows: np.ndarray, gval_rows: Optional[np.ndarray], oracle_ou
                 o = np.where(o >= 0, o - off, o)
             gv = None if gval_rows is None else np.asarray(gval_rows[r, h], np.float64)
             sc = oracle_out["scores"][r][h]
+            mg = oracle_out["mags"][r][h] if "mags" in oracle_out else None
             where = f"{label} row (b={b}, i={i})"
             f = int(oracle_out["kept"][r, h]) if "kept" in oracle_out else 0
             if f:
-                g, gv, sc, o, k_rest = _split_kept(g, gv, sc, o, f, k, tol, where)
+                g, gv, sc, o, k_rest, mg = _split_kept(g, gv, sc, o, f, k, tol, where, mg, budget)
             else:
                 k_rest = k
-            check_row(g, gv, sc, k_rest, tol, oidx=o, stats=st, where=where)
+            check_row(g, gv, sc, k_rest, tol, oidx=o, stats=st, where=where, mag=mg,
+                      budget=budget)
     return st
 
 
-def _split_kept(g, gv, s, o, f, k, tol, where):
+def _split_kept(g, gv, s, o, f, k, tol, where, mag=None, budget=None):
     """Rows with blocks that are always kept: the first f slots must equal the
     oracle's (an index rule, no scores involved), their values within the
     tolerance; the remaining slots are then checked by the rule above over the
@@ -171,6 +206,9 @@ def _split_kept(g, gv, s, o, f, k, tol, where):
         err = np.abs(gv[:f] - s[g[:f]])
         assert (err <= tol * np.maximum(np.abs(s[g[:f]]), floor)).all(), \
             f"{where}: kept block values off by {err.max():.3g}"
+        if mag is not None and budget is not None:
+            assert (err <= budget * U32 * np.asarray(mag)[g[:f]]).all(), \
+                f"{where}: kept block values outside the float32 error budget"
     rest = np.setdiff1d(np.arange(s.shape[0]), g[:f])
     pos = np.full(s.shape[0], -2, np.int64)
     pos[rest] = np.arange(rest.shape[0])
@@ -179,4 +217,5 @@ def _split_kept(g, gv, s, o, f, k, tol, where):
         return np.where(x >= 0, pos[np.clip(x, 0, s.shape[0] - 1)], x)
     gr = renum(g)
     assert (gr != -2).all(), f"{where}: a kept block is returned twice"
-    return gr, (None if gv is None else gv[f:]), s[rest], renum(o), k - f
+    return (gr, (None if gv is None else gv[f:]), s[rest], renum(o), k - f,
+            None if mag is None else np.asarray(mag)[rest])

@@ -83,3 +83,24 @@ def test_floor_follows_the_largest_magnitude():
     check_row(idx, val, s, 3, 2e-2)
     with pytest.raises(AssertionError):       # an error well above the floor still fails
         check_row(idx, np.array([0.0, 0.0, -0.002 + 0.01]), s, 3, 2e-2)
+
+
+def test_float32_error_budget():
+    """Values within budget * 2^-24 * P_j of the exact score pass; a value off
+    by more fails although it is well inside the tolerance; the largest error
+    is recorded in units of 2^-24 P_j."""
+    from tests.checker import U32, RowStats
+    s = _scores(3)
+    p = np.abs(s) * 3 + 1.0
+    idx, val = _exact(s, 10)
+    head = idx[:10]
+    st = RowStats()
+    ok = val.copy()
+    ok[:10] = s[head] + 100 * U32 * p[head]
+    check_row(idx, ok, s, 10, TOL, mag=p, budget=392, stats=st)
+    assert 99 < st.max_err_u < 101
+    bad = val.copy()
+    bad[3] = s[head[3]] + 500 * U32 * p[head[3]]
+    assert abs(bad[3] - s[head[3]]) < TOL * abs(s[head[3]])
+    with pytest.raises(AssertionError):
+        check_row(idx, bad, s, 10, TOL, mag=p, budget=392)

@@ -15,7 +15,7 @@ from oracle import li_oracle as O
 from sparse_attention_top_amd import binding as B
 from sparse_attention_top_amd import indexer as I
 from sparse_attention_top_amd import synth
-from tests.checker import TOL, check_rows, visible_pairs
+from tests.checker import TOL, check_rows, err_budget, visible_pairs
 
 pytestmark = pytest.mark.gpu
 
@@ -43,14 +43,13 @@ def run_and_check(wl, rows=None, return_value=True, label=""):
     gv = _flat_rows(wl, val.cpu().numpy()) if return_value else None
     o = O.run(wl, rows=rows, want_scores=True)
     sel = _row_index(wl, o["rows"])
+    # values are also held to the float32 error bound of the formula
     st = check_rows(gi[sel], None if gv is None else gv[sel], o, wl.sparse_count,
-                    TOL[wl.qk_dtype], label=label or wl.name, offsets=wl.output_idx_offset)
+                    TOL[wl.qk_dtype], label=label or wl.name, offsets=wl.output_idx_offset,
+                    budget=err_budget(wl))
     if rows is None:   # rows the oracle did not visit must not exist
         assert sel.shape[0] == gi.shape[0]
     _say(f"[gpu] {label or wl.name}: {st}")
-    # The GPU's values stay far inside the band floor 2^-6 M tol: the floor is
-    # never what lets a value through.
-    assert st.max_err_m <= TOL[wl.qk_dtype] / 256, f"value error {st.max_err_m:.3g} M"
     return st, idx, val
 
 

@@ -553,3 +553,38 @@ def test_tnd_padding_equals_unpadded(mode):
         rows += used
     assert rows == 19
     _check_structure(pad, o)
+
+
+def test_row_magnitudes_hand_values():
+    """P_j = sum_g |w_g| sum_d |q_gd k_jd| on the shared hand data: with Q = I
+    the per-head absolute dots of K = [[1,1],[2,-1],[-1,3],[-2,-2]] are
+    (1,2,1,2) and (1,1,3,2); W = (1, 0.5) gives (1.5, 2.5, 2.5, 3) and
+    W = (1, -1) gives (2, 3, 4, 4). With scales Sq = (2, 1), Sk = (1, 0.5, 2, 1)
+    and W = (1, 0.5): (2*1 + 0.5*1, 0.5*(2*2 + 0.5*1), 2*(2*1 + 0.5*3),
+    2*2 + 0.5*2) = (2.5, 2.25, 7, 5)."""
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    k = np.array([[1.0, 1.0], [2.0, -1.0], [-1.0, 3.0], [-2.0, -2.0]])
+    assert O.row_magnitudes(q, np.array([1.0, 0.5]), k).tolist() == [1.5, 2.5, 2.5, 3.0]
+    assert O.row_magnitudes(q, np.array([1.0, -1.0]), k).tolist() == [2.0, 3.0, 4.0, 4.0]
+    p = O.row_magnitudes(q, np.array([1.0, 0.5]), k, np.array([2.0, 1.0]),
+                         np.array([1.0, 0.5, 2.0, 1.0]))
+    assert p.tolist() == [2.5, 2.25, 7.0, 5.0]
+    # terms that cancel inside a dot still count: Q = [[1,1],[1,-1]] against
+    # keys (1,1) and (2,-1) has dots (2,1) and (0,3) but term sums (2,3), (2,3)
+    q2 = np.array([[1.0, 1.0], [1.0, -1.0]])
+    assert O.row_magnitudes(q2, np.array([1.0, 1.0]), k[:2]).tolist() == [4.0, 6.0]
+
+
+def test_row_magnitudes_bound_and_equality():
+    """P_j >= |s_j| always (triangle inequality, and ReLU(x) <= |x|), with
+    equality when every q, k and w is non-negative (no term cancels and the
+    ReLU is the identity)."""
+    rng = np.random.default_rng(41)
+    q, k, w = rng.normal(size=(16, 32)), rng.normal(size=(50, 32)), rng.normal(size=16)
+    qs, ks = rng.random(16), rng.random(50)
+    s = O.row_scores(q, w, k, qs, ks)
+    p = O.row_magnitudes(q, w, k, qs, ks)
+    assert (p >= np.abs(s) * (1 - 1e-12)).all() and (p > np.abs(s) * 1.01).any()
+    qa, ka, wa = np.abs(q), np.abs(k), np.abs(w)
+    np.testing.assert_allclose(O.row_magnitudes(qa, wa, ka, qs, ks),
+                               O.row_scores(qa, wa, ka, qs, ks), rtol=1e-13)

@@ -76,6 +76,9 @@ MUTANTS = [
     ("TND keys at the query offsets", "r = int(wl.cu_seqlens_k[b]) + j",
      "r = int(wl.cu_seqlens_q[b]) + j"),
     ("TND queries from the first sequence", "r = int(wl.cu_seqlens_q[b]) + rows", "r = rows"),
+    ("magnitudes keep the weight signs", "return np.abs(w) @ x", "return w @ x"),
+    ("magnitudes of the dot, not of its terms", "x = np.abs(q) @ np.abs(k).T",
+     "x = np.abs(q @ k.T)"),
 ]
 
 
