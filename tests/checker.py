@@ -57,17 +57,26 @@ U32 = 2.0 ** -24   # float32 unit roundoff
 def err_budget(wl) -> float:
     """Error budget c (in units of 2^-24 * P_j) of a float32 evaluation of the
     formula: D-term dot products, an N1-term head sum and a few scale and
-    output roundings, doubled to cover any rounding mode of the accumulators."""
-    return 2.0 * (wl.D + wl.N1 // wl.N2 + 4)
+    output roundings, doubled to cover any rounding mode of the accumulators.
+    For e4m3fn the dot-product term is 8 D: the fp8 matrix instruction sums
+    each step's 64 products in one fused operation that keeps fewer low bits of
+    the smaller products than a float32 sum would (measured on the GPU: up to
+    368 * 2^-24 P_j for D = 64 and one head, against 0.5 for the 16-bit types;
+    exact on inputs whose products share a narrow exponent range, e4m3fn
+    subnormal codes included)."""
+    a = 8 if wl.qk_dtype == "e4m3fn" else 1
+    return 2.0 * (a * wl.D + wl.N1 // wl.N2 + 4)
 
 
 class RowStats:
     """Counts over the checked rows, plus two guards on the band floor:
     max_err_u, the largest |v_j - s_j| / (2^-24 P_j) over every returned value
     (bounded by the error budget when one is given), max_err_m, the same error
-    over the row's largest score magnitude M, and floor_rows, the rows that
-    would fail one of rules 2-5 if the floor 2^-6 M were dropped
-    (tau = tol * |s_(k)|)."""
+    over the row's largest score magnitude M, and the rows that would fail if
+    the floor 2^-6 M were dropped (tau = tol * |s_(k)|): floor_sel for the
+    selection (rules 2-4), floor_val for the values (rule 5; a value near zero
+    whose terms cancel has a large error relative to itself, which the float32
+    budget above bounds instead)."""
 
     def __init__(self):
         self.rows = 0
@@ -76,12 +85,14 @@ class RowStats:
         self.all_keys = 0
         self.max_err_u = 0.0
         self.max_err_m = 0.0
-        self.floor_rows = 0
+        self.floor_sel = 0
+        self.floor_val = 0
 
     def __repr__(self):
         return (f"rows={self.rows} exact_set={self.exact_set} tie_band={self.in_band} "
                 f"all_keys={self.all_keys} max_err/(u*P)={self.max_err_u:.3g} "
-                f"max_err/M={self.max_err_m:.3g} floor_rows={self.floor_rows}")
+                f"max_err/M={self.max_err_m:.3g} floor_sel={self.floor_sel} "
+                f"floor_val={self.floor_val}")
 
 
 def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: int,
@@ -106,7 +117,7 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
     srt = np.sort(s)[::-1]
     s1 = np.abs(s).max()
     floor = 2.0 ** -6 * s1
-    needs_floor = False
+    needs_sel = needs_val = False
     if n <= k:
         assert np.array_equal(np.sort(head), np.arange(n)), f"{where}: must return every key"
         tau = tol * max(abs(srt[-1]), floor)
@@ -123,8 +134,8 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
         missing = np.setdiff1d(must, head)
         assert missing.size == 0, f"{where}: missing clear winners {missing[:5]}"
         tau0 = tol * abs(sk)
-        needs_floor |= bool((sel < sk - tau0).any())
-        needs_floor |= np.setdiff1d(np.nonzero(s > sk + tau0)[0], head).size > 0
+        needs_sel |= bool((sel < sk - tau0).any())
+        needs_sel |= np.setdiff1d(np.nonzero(s > sk + tau0)[0], head).size > 0
         if stats is not None:
             if oidx is not None and np.array_equal(np.sort(head), np.sort(oidx[:m])):
                 stats.exact_set += 1
@@ -134,6 +145,8 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
     sh = s[head]
     band = tol * np.maximum(np.abs(sh), floor)
     assert (sh[1:] <= sh[:-1] + band[:-1] + band[1:]).all(), f"{where}: not sorted by score"
+    band0 = tol * np.abs(sh)
+    needs_sel |= not (sh[1:] <= sh[:-1] + band0[:-1] + band0[1:]).all()
     if gval is not None:
         gval = np.asarray(gval, dtype=np.float64)
         v, vt = gval[:m], gval[m:]
@@ -143,7 +156,7 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
         assert (err <= lim).all(), f"{where}: values off by up to {err.max():.3g} " \
                                    f"(limit {lim[np.argmax(err - lim)]:.3g})"
         assert (np.diff(v) <= 0).all(), f"{where}: values not non-increasing"
-        needs_floor |= bool((err > tol * np.abs(sh)).any())
+        needs_val |= bool((err > tol * np.abs(sh)).any())
         if mag is not None:
             pm = np.asarray(mag, np.float64)[head]
             eu = np.where(pm > 0, err / (U32 * np.where(pm > 0, pm, 1.0)),
@@ -156,8 +169,9 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
                 stats.max_err_u = max(stats.max_err_u, float(eu.max()))
         if stats is not None and s1 > 0:
             stats.max_err_m = max(stats.max_err_m, float(err.max() / s1))
-    if stats is not None and needs_floor:
-        stats.floor_rows += 1
+    if stats is not None:
+        stats.floor_sel += int(needs_sel)
+        stats.floor_val += int(needs_val)
 
 
 def check_rows(gidx_rows: np.ndarray, gval_rows: Optional[np.ndarray], oracle_out: dict,

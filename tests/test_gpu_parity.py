@@ -360,6 +360,54 @@ def test_integer_inputs_bit_exact(dt, mode, extra):
     assert np.array_equal(gv, ov), "values differ from the oracle on exact inputs"
 
 
+def _fp8_exact_workload(q_codes, k_codes, N1, D, seed, layout="TND", **extra):
+    """e4m3fn problem whose every score is exact in fp32: codes drawn from the
+    given value sets (exactly representable), unit dequant scales and weights
+    that are multiples of 1/8 in [-1/2, 1/2]."""
+    rng = np.random.default_rng(seed)
+    kw = dict(layout_q=layout, layout_k=layout, qk_dtype="e4m3fn", w_dtype="f32", N1=N1, D=D,
+              seqlens_q=[40, 3], seqlens_k=[40, 700], sparse_count=64, sparse_mode=3,
+              seed=seed)
+    kw.update(extra)
+    wl = synth.build("fp8_exact", **kw)
+    wl.q = synth.encode_e4m3fn(rng.choice(q_codes, wl.q.shape).astype(np.float32))
+    wl.k = synth.encode_e4m3fn(rng.choice(k_codes, wl.k.shape).astype(np.float32))
+    wl.q_scale = np.ones_like(wl.q_scale)
+    wl.k_scale = np.ones_like(wl.k_scale)
+    wl.w = (rng.integers(-4, 5, wl.w.shape) / 8.0).astype(np.float32)
+    return wl
+
+
+_SMALL_INTS = np.arange(-3, 4, dtype=np.float64)
+# every e4m3fn subnormal: m * 2^-9, m = -7..7 (exponent field 0)
+_E4M3_SUBNORMALS = np.arange(-7, 8, dtype=np.float64) * 2.0 ** -9
+
+
+@pytest.mark.parametrize("case", ["ints_d128_n64", "ints_d64_n1", "subnormal_q_d64_n1",
+                                  "subnormal_q_d128_n64", "subnormal_both_d128_n8"])
+def test_fp8_exact_inputs_bit_exact(case):
+    """fp8 scores that are exact in fp32 (small integers, and e4m3fn subnormal
+    codes times small integers or times each other: every product and partial
+    sum is a multiple of 2^-18 well inside float32's range) must come out of the
+    fp8 matrix cores bit for bit: subnormal codes are decoded, not flushed."""
+    q_codes, k_codes, N1, D = {
+        "ints_d128_n64": (_SMALL_INTS, _SMALL_INTS, 64, 128),
+        "ints_d64_n1": (_SMALL_INTS, _SMALL_INTS, 1, 64),
+        "subnormal_q_d64_n1": (_E4M3_SUBNORMALS, _SMALL_INTS, 1, 64),
+        "subnormal_q_d128_n64": (_E4M3_SUBNORMALS, _SMALL_INTS, 64, 128),
+        "subnormal_both_d128_n8": (_E4M3_SUBNORMALS, _E4M3_SUBNORMALS, 8, 128),
+    }[case]
+    wl = _fp8_exact_workload(q_codes, k_codes, N1, D, seed=zlib.crc32(case.encode()))
+    idx, val, _, _ = I.run_workload(wl, DEV, return_value=True)
+    oi, ov = O.run_full(wl)
+    gi, gv = idx.cpu().numpy(), val.cpu().numpy()
+    diff = np.nonzero(gv != ov)
+    _say(f"[gpu] fp8 exact {case}: {diff[0].shape[0]} values differ; first: "
+         f"{[(float(gv[d]), float(ov[d])) for d in zip(*diff)][:4]}")
+    assert np.array_equal(gv, ov), "values differ from the oracle on exact fp8 inputs"
+    assert np.array_equal(gi, oi), "indices differ from the oracle on exact fp8 inputs"
+
+
 @pytest.mark.parametrize("sk,k", [(3000, 2048), (20000, 2048), (40000, 2048), (5000, 4096),
                                   (9000, 8192), (40000, 8192)])
 def test_zero_weights_long_rows_use_exact_fallback(sk, k):
