@@ -300,6 +300,29 @@ li_status li_indexer(const li_problem* p, const li_inputs* in, const void* meta_
                      const void* meta_dev, void* ws, size_t ws_bytes,
                      int32_t* sparse_indices, float* sparse_values, void* stream);
 
+/*
+ * li_indexer_noalloc -- li_indexer without a caller workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The call allocates nothing;
+ * its workspace is a device array inside the library of li_noalloc_capacity()
+ * bytes (256 MiB: an 8K x 8K causal prefill fits), held by every GPU the
+ * library runs on until the process ends.
+ *  Arguments as for li_indexer, without ws / ws_bytes.
+ * Errors: as for li_indexer; LI_ERR_WORKSPACE_TOO_SMALL (nothing enqueued)
+ * when li_workspace_size() of the problem exceeds the capacity; LI_ERR_HIP if
+ * the array's device address cannot be obtained.
+ * All calls on one GPU share that GPU's array: calls that may overlap on one
+ * GPU (different streams or threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe. Nothing in the array needs to
+ * be cleared between calls.
+ */
+li_status li_indexer_noalloc(const li_problem* p, const li_inputs* in, const void* meta_host,
+                             const void* meta_dev, int32_t* sparse_indices,
+                             float* sparse_values, void* stream);
+
+/* Bytes of the device array li_indexer_noalloc uses as its workspace. */
+size_t li_noalloc_capacity(void);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char* li_last_error(void);
 

@@ -148,7 +148,11 @@ def lib() -> ctypes.CDLL:
         L.li_score.argtypes = [P(li_problem), P(li_inputs), vp, vp, vp, sz, vp]
         L.li_topk.argtypes = [P(li_problem), vp, vp, vp, sz, vp, vp, vp]
         L.li_indexer.argtypes = [P(li_problem), P(li_inputs), vp, vp, vp, sz, vp, vp, vp]
-        for f in ("li_metadata", "li_workspace_size", "li_score", "li_topk", "li_indexer"):
+        L.li_indexer_noalloc.argtypes = [P(li_problem), P(li_inputs), vp, vp, vp, vp, vp]
+        L.li_noalloc_capacity.argtypes = []
+        L.li_noalloc_capacity.restype = sz
+        for f in ("li_metadata", "li_workspace_size", "li_score", "li_topk", "li_indexer",
+                  "li_indexer_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.li_last_error.argtypes = []
         L.li_last_error.restype = ctypes.c_char_p
@@ -233,6 +237,17 @@ def li_indexer(p: li_problem, inputs: li_inputs, meta_host: np.ndarray, meta_dev
     _check(lib().li_indexer(ctypes.byref(p), ctypes.byref(inputs), meta_host.ctypes.data,
                             meta_dev or None, ws or None, int(ws_bytes), sparse_indices or None,
                             sparse_values or None, stream or None))
+
+
+def li_indexer_noalloc(p: li_problem, inputs: li_inputs, meta_host: np.ndarray, meta_dev: int,
+                       sparse_indices: int, sparse_values: int = 0, stream: int = 0) -> None:
+    _check(lib().li_indexer_noalloc(ctypes.byref(p), ctypes.byref(inputs), meta_host.ctypes.data,
+                                    meta_dev or None, sparse_indices or None,
+                                    sparse_values or None, stream or None))
+
+
+def li_noalloc_capacity() -> int:
+    return int(lib().li_noalloc_capacity())
 
 
 # Layout of the task table header (mirrors MetaHeader in csrc/li_internal.h),

@@ -22,13 +22,18 @@ namespace {
 
 thread_local std::string g_last_error;
 
-li_status fail(li_status st, const char* fmt, ...) {
+li_status vfail(li_status st, const char* fmt, va_list ap) {
   char buf[512];
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  g_last_error = buf;
+  return st;
+}
+
+li_status fail(li_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  vfail(st, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return st;
 }
 
@@ -179,6 +184,15 @@ const T* meta_ptr(const void* base, uint64_t off) {
 }
 
 }  // namespace
+
+li_status set_error(li_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(st, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
 }  // namespace li
 
 using namespace li;

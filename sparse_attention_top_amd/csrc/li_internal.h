@@ -186,6 +186,9 @@ hipError_t launch_score(const li_problem& p, int variant, int num_items, const S
                         hipStream_t s);
 hipError_t launch_topk(const li_problem& p, const TopkArgs& a, hipStream_t s);
 
+// Records the message li_last_error() returns on this thread and returns st.
+li_status set_error(li_status st, const char* fmt, ...);
+
 // Visible keys of query row i (i < s_q) of a sequence with lengths (s_q, s_k):
 // mode 0 every key; mode 3 the right-down causal rule j <= i + S_k - S_q. With
 // compressed keys (ratio r, residual res) the sequence has L = s_k*r + res

@@ -25,7 +25,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(ROOT, "include", "li.h")).read()
-    names = sorted(set(re.findall(r"^\s*(?:li_status|const char\*|int32_t)\s+(li_\w+)\s*\(",
+    names = sorted(set(re.findall(r"^\s*(?:li_status|const char\*|int32_t|size_t)\s+(li_\w+)\s*\(",
                                   hdr, re.M)))
     assert {"li_metadata", "li_workspace_size", "li_score", "li_topk", "li_indexer",
             "li_last_error", "li_api_version"} <= set(names)
