@@ -19,9 +19,10 @@
 //
 // Fast path (any row whose scores spread over a finite range):
 //   1. min / max of the row (block reduction);
-//   2. histogram over 4096 buckets linear in the score between min and max
+//   2. histogram over nb buckets linear in the score between min and max
 //      (monotone in the score, so bucket order is score order; the buckets follow
-//      the data's range, so they stay short);
+//      the data's range, so they stay short); nb is the row length rounded up
+//      to a power of two, at most 4096;
 //   3. a block scan from the top bucket down finds the bucket t holding the k-th
 //      largest and turns the counts into each bucket's output offset;
 //   4. every key in a bucket >= t is written to its bucket's segment in LDS
@@ -131,13 +132,17 @@ template <bool W16> constexpr int kCounterWords = W16 ? kBuckets / 2 : kBuckets;
 
 template <int NT, bool W16, int KMAX>
 struct Smem {
-  alignas(16) uint32_t cnt[kCounterWords<W16>];   // histogram, offsets; radix digits
+  // histogram, offsets; radix digits. The word past the buckets stays zero: it
+  // is the end of the (empty) segment above the top bucket.
+  alignas(16) uint32_t cnt[kCounterWords<W16> + 4];
   unsigned long long buf[KMAX + kSegMax + kBufPad];  // composites grouped by bucket
   uint32_t s_wave[NT / 64];
   float s_red[2 * (NT / 64)];
   uint32_t s_sel[4];
 };
 static_assert(kBuckets / 2 >= kRadixBins, "radix digits reuse the histogram words");
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 template <bool W16>
 struct Counters {
@@ -147,13 +152,31 @@ struct Counters {
     if constexpr (W16) return (word(b >> 1) >> ((b & 1) << 4)) & 0xFFFFu;
     else return word(b);
   }
+  // (get(b + 1), get(b)) from the two adjacent words that hold them.
+  __device__ void get_pair(int b, uint32_t& up, uint32_t& at) const {
+    if constexpr (W16) {
+      const uint32_t w0 = word(b >> 1), w1 = word((b >> 1) + 1);
+      const bool odd = (b & 1) != 0;
+      at = odd ? w0 >> 16 : w0 & 0xFFFFu;
+      up = odd ? w1 & 0xFFFFu : w0 >> 16;
+    } else {
+      at = word(b);
+      up = word(b + 1);
+    }
+  }
   __device__ void add(int b) const {
     if constexpr (W16) atomicAdd(&word(b >> 1), 1u << ((b & 1) << 4));
     else atomicAdd(&word(b), 1u);
   }
-  __device__ uint32_t fetch_add(int b) const {
-    if constexpr (W16) return (atomicAdd(&word(b >> 1), 1u << ((b & 1) << 4)) >> ((b & 1) << 4)) & 0xFFFFu;
+  // fetch_add split in two, so that several atomics can be in flight before the
+  // first result is used: the raw old word, then the bucket's old count in it.
+  __device__ uint32_t fetch_add_raw(int b) const {
+    if constexpr (W16) return atomicAdd(&word(b >> 1), 1u << ((b & 1) << 4));
     else return atomicAdd(&word(b), 1u);
+  }
+  __device__ uint32_t field(uint32_t raw, int b) const {
+    if constexpr (W16) return (raw >> ((b & 1) << 4)) & 0xFFFFu;
+    else return raw;
   }
 };
 
@@ -179,13 +202,15 @@ __device__ inline T wave_scan(T x, T id, Op op) {
   return x;
 }
 
-// Exclusive prefix sum over the block in thread order.
+// Exclusive prefix sum over the block in thread order. Waves from nw_act on
+// must hold v = 0; they skip their scan.
 template <int NT>
-__device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave) {
+__device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, int nw_act = NT / 64) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const uint32_t x = wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+  uint32_t x = 0;
+  if (wave < nw_act) x = wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   uint32_t before = 0;
@@ -215,16 +240,13 @@ __device__ inline void block_minmax(float& lo, float& hi, float* s_red) {
   }
 }
 
-// Monotone map of [lo, hi] onto bucket indices 0..kBuckets-1 (one rounding, so
-// every pass computes the same bucket for the same score). The clamp covers
-// both ends: when |lo| is large against the range, the rounded offset can put
-// lo slightly outside [0, kBuckets).
+// Monotone map of [lo, hi] onto bucket indices 0..nb-1: floor((x - lo) * scale)
+// with scale = (nb - 1/2) / (hi - lo). x - lo rounds to a value in [0, hi - lo]
+// (rounding is monotone and exact at 0), and (hi - lo) * scale rounds below nb,
+// so no clamp is needed; every pass computes the same bucket for a score.
 struct Bucketing {
-  float scale, off;
-  __device__ int operator()(float x) const {
-    const int b = (int)fmaf(x, scale, off);
-    return min(max(b, 0), kBuckets - 1);
-  }
+  float scale, lo;
+  __device__ int operator()(float x) const { return (int)((x - lo) * scale); }
 };
 
 // Which keys of a float4 group starting at key j0 take part: e in [beg, end)
@@ -352,31 +374,45 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   const int n = row.count();
   const float range = hi - lo;
   if (!(hi > lo) || !(range <= 3.0e38f)) return false;
-  const float scale = (float)kBuckets / range;
+  // nb buckets: the row length rounded up to a power of two, between one
+  // wave's share and kBuckets. Short rows then scan fewer buckets (only the
+  // waves that own buckets take part) while their segments stay short; rows of
+  // 2K-4K keys keep kBuckets (halving them there lengthened the segments and
+  // cost 7% on such rows).
+  constexpr int BPT = kBuckets / NT;        // buckets per active thread
+  constexpr int BPW = W16 ? 2 : 1;          // buckets per counter word
+  constexpr int WPT = BPT / BPW;
+  static_assert(BPT % 2 == 0, "whole 16-bit counter pairs per thread");
+  constexpr int NB_MIN = BPT * 64;          // the buckets of one wave
+  int nb = NB_MIN;
+  while (nb < kBuckets && nb < n) nb <<= 1;   // uniform
+  const float scale = ((float)nb - 0.5f) / range;
   if (!(scale <= 3.0e38f)) return false;
-  const Bucketing bucket{scale, -lo * scale};
+  const Bucketing bucket{scale, lo};
   const Counters<W16> cnt{sm.cnt};
 
   row.each([&](float x, int) { cnt.add(bucket(x)); });
   __syncthreads();
 
-  // Thread t owns the counter words of buckets kBuckets-1 - (t*BPT + q), a
-  // descending run of WPT words kept in registers through the scan.
-  constexpr int BPT = kBuckets / NT;
-  constexpr int BPW = W16 ? 2 : 1;          // buckets per counter word
-  constexpr int WPT = BPT / BPW;
-  static_assert(BPT % 2 == 0, "whole 16-bit counter pairs per thread");
+  // Active thread t (t * BPT < nb; whole waves) owns buckets nb-1 - (t*BPT + q),
+  // a descending run of WPT words kept in registers through the scan.
+  const bool act = tid * BPT < nb;              // uniform per wave
+  const int nw_act = nb / NB_MIN;
   // word of the thread's q-th bucket pair (descending): covers buckets
-  // kBuckets-1 - (tid*BPT + BPW*q) and, for W16, the one below it
-  const int w_top = kCounterWords<W16> - 1 - tid * WPT;
+  // nb-1 - (tid*BPT + BPW*q) and, for W16, the one below it
+  const int w_top = nb / BPW - 1 - tid * WPT;
   uint32_t word[WPT];
   uint32_t local = 0;
 #pragma unroll
-  for (int q = 0; q < WPT; ++q) {
-    word[q] = cnt.word(w_top - q);
-    local += W16 ? (word[q] >> 16) + (word[q] & 0xFFFFu) : word[q];
+  for (int q = 0; q < WPT; ++q) word[q] = 0;
+  if (act) {
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      word[q] = cnt.word(w_top - q);
+      local += W16 ? (word[q] >> 16) + (word[q] & 0xFFFFu) : word[q];
+    }
   }
-  const uint32_t before = block_exclusive_scan<NT>(local, sm.s_wave);
+  const uint32_t before = block_exclusive_scan<NT>(local, sm.s_wave, nw_act);
   // Counts in descending bucket order: for W16 the high half (odd bucket) first.
   auto count_at = [&](int q, int h) -> uint32_t {   // h = 0: higher bucket of the word
     if constexpr (W16) return h == 0 ? word[q] >> 16 : word[q] & 0xFFFFu;
@@ -387,7 +423,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
       sm.s_sel[0] = 0u;           // every bucket is taken whole
       sm.s_sel[1] = 0xFFFFFFFFu;
     }
-  } else if (before < (uint32_t)K && (uint32_t)K <= before + local) {
+  } else if (act && before < (uint32_t)K && (uint32_t)K <= before + local) {
     uint32_t cum = before;
 #pragma unroll
     for (int q = 0; q < WPT; ++q)
@@ -395,7 +431,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
       for (int h = 0; h < BPW; ++h) {
         const uint32_t c = count_at(q, h);
         if (cum < (uint32_t)K && (uint32_t)K <= cum + c) {
-          sm.s_sel[0] = (uint32_t)(kBuckets - 1 - (tid * BPT + BPW * q + h));
+          sm.s_sel[0] = (uint32_t)(nb - 1 - (tid * BPT + BPW * q + h));
           sm.s_sel[1] = (uint32_t)K - cum;
         }
         cum += c;
@@ -404,46 +440,79 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   __syncthreads();
   const int t = (int)sm.s_sel[0];
   const uint32_t need = sm.s_sel[1];
-  // Counts become exclusive offsets from the top bucket (16-bit fields are each
-  // written on their own, so a field that wraps below t cannot spill into its
-  // neighbour; only buckets >= t are used, and their offsets stay below
-  // K + kSegMax). Track the largest segment at or above t.
-  uint32_t cum = before, big = 0;
+  // Counts become exclusive offsets from the top bucket for the threads that
+  // own buckets >= t (16-bit fields are each written on their own, so a field
+  // that wraps below t cannot spill into its neighbour; only buckets >= t are
+  // used, and their offsets stay below K + kSegMax). Track the largest segment
+  // at or above t.
+  if (act && nb - 1 - tid * BPT >= t) {
+    uint32_t cum = before, big = 0;
 #pragma unroll
-  for (int q = 0; q < WPT; ++q) {
-    const int b_hi = kBuckets - 1 - (tid * BPT + BPW * q);
-    if constexpr (W16) {
-      const uint32_t c_hi = count_at(q, 0), c_lo = count_at(q, 1);
-      cnt.word(w_top - q) = ((cum & 0xFFFFu) << 16) | ((cum + c_hi) & 0xFFFFu);
-      cum += c_hi + c_lo;
-      if (b_hi >= t && c_hi > big) big = c_hi;
-      if (b_hi - 1 >= t && c_lo > big) big = c_lo;
-    } else {
-      const uint32_t c = count_at(q, 0);
-      cnt.word(w_top - q) = cum;
-      cum += c;
-      if (b_hi >= t && c > big) big = c;
+    for (int q = 0; q < WPT; ++q) {
+      if constexpr (W16) {
+        const uint32_t c_hi = count_at(q, 0), c_lo = count_at(q, 1);
+        cnt.word(w_top - q) = ((cum & 0xFFFFu) << 16) | ((cum + c_hi) & 0xFFFFu);
+        cum += c_hi + c_lo;
+      } else {
+        cnt.word(w_top - q) = cum;
+        cum += count_at(q, 0);
+      }
     }
+    if (nb - BPT - tid * BPT >= t) {
+      // every bucket of the thread is at or above t: the largest count, two
+      // 16-bit fields at a time
+      if constexpr (W16) {
+        uint32_t mx = word[0];
+#pragma unroll
+        for (int q = 1; q < WPT; ++q) mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+            __builtin_bit_cast(u16x2_t, mx), __builtin_bit_cast(u16x2_t, word[q])));
+        big = max(mx >> 16, mx & 0xFFFFu);
+      } else {
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) big = max(big, word[q]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < WPT; ++q) {
+        const int b_hi = nb - 1 - (tid * BPT + BPW * q);
+        if constexpr (W16) {
+          const uint32_t c_hi = count_at(q, 0), c_lo = count_at(q, 1);
+          if (b_hi >= t && c_hi > big) big = c_hi;
+          if (b_hi - 1 >= t && c_lo > big) big = c_lo;
+        } else {
+          const uint32_t c = count_at(q, 0);
+          if (b_hi >= t && c > big) big = c;
+        }
+      }
+    }
+    if (big > (uint32_t)kSegMax) atomicMax(&sm.s_sel[2], big);
   }
-  if (big > (uint32_t)kSegMax) atomicMax(&sm.s_sel[2], big);
   __syncthreads();
   if (sm.s_sel[2] != 0u) return false;
 
   // Counting sort of the keys of buckets >= t into their bucket segments.
-  // Afterwards bucket b's segment is [end(b+1), end(b)) (end(kBuckets) = 0).
+  // Afterwards bucket b's segment is [end(b+1), end(b)) (end(nb) = 0: the zero
+  // word past the buckets). The four atomics of a group are all issued before
+  // their results are read.
   row.each4([&](const float (&x)[4], int j0, auto rng) {
     int b[4];
-    uint32_t pos[4];
+    bool c[4];
+    uint32_t raw[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {   // all four fetch-adds in flight before any write
+    for (int e = 0; e < 4; ++e) {
       b[e] = bucket(x[e]);
-      if (rng.ok(e) && b[e] >= t) pos[e] = cnt.fetch_add(b[e]);
+      c[e] = rng.ok(e) && b[e] >= t;
+      raw[e] = 0;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (rng.ok(e) && b[e] >= t) {
-        if constexpr (W16) sm.buf[pos[e]] = bucket_composite(x[e], b[e], j0 + e);
-        else sm.buf[pos[e]] = composite(x[e], j0 + e);
+      if (c[e]) raw[e] = cnt.fetch_add_raw(b[e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c[e]) {
+        const uint32_t pos = cnt.field(raw[e], b[e]);
+        if constexpr (W16) sm.buf[pos] = bucket_composite(x[e], b[e], j0 + e);
+        else sm.buf[pos] = composite(x[e], j0 + e);
       }
   });
   __syncthreads();
@@ -470,8 +539,11 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     for (int u = 0; u < 4; ++u) {
       if constexpr (W16) bk[u] = bucket_of(me[u]);
       else bk[u] = bucket(from_ord((uint32_t)(me[u] >> 32)));
-      s0[u] = bk[u] == kBuckets - 1 ? 0u : cnt.get(bk[u] + 1);
-      s1[u] = p0 + u * NT < ncand ? cnt.get(bk[u]) : s0[u];
+      cnt.get_pair(bk[u], s0[u], s1[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (p0 + u * NT >= ncand) s1[u] = s0[u];
       rank[u] = 0;
       len = max(len, s1[u] - s0[u]);
     }
