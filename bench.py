@@ -12,7 +12,8 @@ Prints ONE JSON line. `value` is indexed query tokens per second; the line
 also carries the score kernel's TFLOP/s against the MFMA peak (or its GB/s
 against HBM when the workload is bandwidth-bound), the top-k kernel's GB/s,
 a `roofline` object for the dominant kernel and a `cpu_baseline` object: the
-fp64 CPU oracle timed on a bounded random sample of the same rows on this host.
+plain C++ fp64 CPU oracle (one thread per available core) timed on a bounded
+random sample of the same rows on this host.
 
 Timing: after W eager warmup steps, K steps (li_score + li_topk each) are
 captured as one HIP graph, replayed once untimed and once between two HIP
@@ -64,25 +65,35 @@ def algorithmic_score_bytes(wl, pairs):
     return b + 4 * int(pairs)
 
 
-def cpu_baseline(wl, seconds, seed=1234):
-    import numpy as np
-    from threadpoolctl import threadpool_info
+def host_threads():
+    """Threads the CPU baseline may use: the process's CPU share (affinity, and
+    OMP_NUM_THREADS where the host sets it)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(omp))) if omp.isdigit() and int(omp) > 0 else max(1, n)
 
-    from oracle import li_oracle as O
+
+def cpu_baseline(wl, seconds, seed=1234):
+    """The plain C++17 fp64 oracle (one std::thread per core) on a random sample
+    of the workload's rows, for about `seconds` of wall time."""
+    import numpy as np
+
+    from oracle import liref
     rows = [(b, i) for b in range(wl.B) for i in range(int(wl.seqlens_q[b]))]
     order = np.random.default_rng(seed).permutation(len(rows))
-    done, t0 = 0, time.perf_counter()
-    chunk = 16
+    threads = host_threads()
+    chunk = 4 * threads
+    done, used, t0 = 0, threads, time.perf_counter()
     while done < len(rows) and time.perf_counter() - t0 < seconds:
         sel = [rows[j] for j in order[done:done + chunk]]
-        O.run(wl, rows=sel)
+        _, _, used = liref.run(wl, rows=sel, nthreads=threads)
         done += len(sel)
     el = time.perf_counter() - t0
-    threads = [t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"]
-    return {"value": done / el, "unit": "tokens/s", "cores": int(max(threads or [1])),
-            "kind": "oracle",
+    return {"value": done / el, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
             "sample": f"{done} query rows drawn uniformly at random (seed {seed}) from the "
-                      f"{len(rows)} rows of the same workload, {el:.1f} s of fp64 oracle time"}
+                      f"{len(rows)} rows of the same workload, {el:.1f} s of the C++ fp64 "
+                      f"oracle on {used} threads (host: {os.cpu_count()} CPUs, "
+                      f"{host_threads()} available)"}
 
 
 def main():
