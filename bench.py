@@ -107,6 +107,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--eager", action="store_true",
                     help="launch every step eagerly instead of replaying captured graphs")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="launches of each kernel timed after a 512 MiB cache flush (0: none)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the on-box reference rates (device copy, bf16 GEMM)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -217,6 +221,58 @@ def main():
     print(f"[bench] timed {K} steps: {ms_per_step:.3f} ms/step (score {score_ms:.3f}, "
           f"top-k {topk_ms:.3f})", flush=True, file=sys.stderr)
 
+    # Cold timings: each launch follows a 512 MiB fill kernel (twice the 256 MB
+    # Infinity Cache plus every L2), so its inputs come from HBM; HIP events on
+    # the launch stream bracket the kernel alone. Median over the launches.
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+
+        def cold_ms(fn):
+            ts = []
+            for r in range(args.cold_reps):
+                flush.fill_(float(r))
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ts.sort()
+            return ts[len(ts) // 2]
+
+        cold = {"score_ms": cold_ms(score), "topk_ms": cold_ms(topk)}
+        del flush
+        print(f"[bench] cold (after a 512 MiB flush): score {cold['score_ms']:.3f} ms, "
+              f"top-k {cold['topk_ms']:.3f} ms", flush=True, file=sys.stderr)
+
+    # On-box reference rates next to the spec peaks: a 1 GiB device copy and a
+    # bf16 8192^3 GEMM (torch library calls; context only, not the indexer).
+    peaks = None
+    if not args.no_peaks:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        m = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        n = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+
+        def rate(fn, reps):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps * 1e-3
+
+        t_copy = rate(lambda: b.copy_(a), 10)
+        t_gemm = rate(lambda: torch.matmul(m, n), 10)
+        peaks = {"device_copy_gbs": round(2 * a.numel() * 4 / t_copy / 1e9, 1),
+                 "bf16_gemm_tflops": round(2 * 8192 ** 3 / t_gemm / 1e12, 1)}
+        del a, b, m, n
+
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -283,6 +339,15 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if cold is not None:
+        out["cold"] = {"score_ms": round(cold["score_ms"], 4), "topk_ms": round(cold["topk_ms"], 4),
+                       "score_tflops": round(flops / (cold["score_ms"] * 1e-3) / 1e12, 1),
+                       "topk_gbs": round(tbytes / (cold["topk_ms"] * 1e-3) / 1e9, 1),
+                       "topk_frac_hbm_peak": round(tbytes / (cold["topk_ms"] * 1e-3) / 1e9 /
+                                                   PEAK_HBM_GBS, 4),
+                       "flush_bytes": 1 << 29, "launches": args.cold_reps, "timing": "eager, median"}
+    if peaks is not None:
+        out["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", flush=True, file=sys.stderr)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
