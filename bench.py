@@ -23,6 +23,13 @@ topk_ms, and the roofline's achieved rate). --eager times K eagerly launched
 steps instead. The defaults (200 warmup steps, 200 timed steps: about 0.2 s of
 GPU work on the headline workload) time the kernels at the clocks they settle
 to under load; a few steps after a cold start read 2-3% slower.
+
+Cold timings (`cold` in the JSON line): each kernel is also launched
+--cold-reps times right after a 512 MiB fill kernel that evicts the Infinity
+Cache and every L2, HIP events on the launch stream around the kernel alone;
+the median is reported with the HBM fraction it implies. `measured_peaks`
+gives this box's own device-copy rate and hipBLASLt bf16 GEMM rate (torch
+library calls, context for the spec peaks only).
 """
 import argparse
 import hashlib
