@@ -30,6 +30,8 @@
 //   5. each such key's rank inside its segment (a count of larger composites)
 //      gives its final sorted position, where it is stored; keys of bucket t
 //      ranked past what is still needed are dropped.
+// Scores are canonicalised as they are read (x + 0: -0 becomes +0, and min /
+// max then need no NaN quieting).
 // Fallback (zero or non-finite range, or a bucket >= t holding more than
 // kSegMax keys, e.g. many equal scores): MSD radix select over the composite
 // with 11/11/10-bit digits (score first, index digits only on ties at the
@@ -71,6 +73,30 @@ constexpr int kBufPad = kSegMax + 4;
 // -0 -> +0 (IEEE: -0 + +0 = +0; every other value is unchanged).
 __device__ inline float canon(float x) { return x + 0.0f; }
 
+// min / max as single instructions. The compiler's fminf / fmaxf first quiet
+// signalling NaNs in every operand it cannot prove canonical (one more
+// instruction per operand); scores here are canonical already (read as x + 0).
+__device__ inline float min_raw(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ inline float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ inline float min3_raw(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ inline float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ inline uint32_t ord_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   const uint32_t flip = (uint32_t)((int32_t)u >> 31) | 0x80000000u;
@@ -93,12 +119,13 @@ __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFF
 
 // The fast path's composite for rows of at most 2^20 keys also carries the
 // key's bucket b in the top 12 bits of its low word: (ord(score), b, 2^20-1-j).
+// s is canonical (read through Row).
 // Inside a bucket segment the order is the plain composite's (b is common);
 // a key of a lower bucket has a lower score, so its composite is lower whatever
 // its low word holds.
 constexpr uint32_t kIdxMask = (1u << 20) - 1;
 __device__ inline unsigned long long bucket_composite(float s, int b, int j) {
-  return ((unsigned long long)ord_bits(canon(s)) << 32) |
+  return ((unsigned long long)ord_bits(s) << 32) |
          (unsigned long long)(((uint32_t)b << 20) | (kIdxMask - (uint32_t)j));
 }
 __device__ inline int bucket_of(unsigned long long c) { return (int)((uint32_t)c >> 20); }
@@ -223,8 +250,8 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, in
 template <int NT>
 __device__ inline void block_minmax(float& lo, float& hi, float* s_red) {
   constexpr int NW = NT / 64;
-  lo = wave_scan(lo, __builtin_huge_valf(), [](float a, float b) { return fminf(a, b); });
-  hi = wave_scan(hi, -__builtin_huge_valf(), [](float a, float b) { return fmaxf(a, b); });
+  lo = wave_scan(lo, __builtin_huge_valf(), [](float a, float b) { return min_raw(a, b); });
+  hi = wave_scan(hi, -__builtin_huge_valf(), [](float a, float b) { return max_raw(a, b); });
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 63) {
     s_red[wave] = lo;
@@ -235,8 +262,8 @@ __device__ inline void block_minmax(float& lo, float& hi, float* s_red) {
   hi = s_red[NW];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
-    lo = fminf(lo, s_red[w]);
-    hi = fmaxf(hi, s_red[NW + w]);
+    lo = min_raw(lo, s_red[w]);
+    hi = max_raw(hi, s_red[NW + w]);
   }
 }
 
@@ -254,7 +281,8 @@ struct Bucketing {
 template <bool KEPT>
 struct GroupRange {
   int beg, end;
-  __device__ bool ok(int e) const { return (!KEPT || e >= beg) && e < end; }
+  bool full;   // uniform: every key of the group takes part
+  __device__ bool ok(int e) const { return full || ((!KEPT || e >= beg) && e < end); }
 };
 
 // The row's scores; keys [lo, n) take part in the selection (lo > 0 only with
@@ -284,10 +312,10 @@ struct Row {
       for (int v = 0; v < R / 4; ++v) {
         if (4 * NT * v >= n) break;   // uniform
         const float4 g = group(threadIdx.x + NT * v);
-        x[4 * v] = g.x;
-        x[4 * v + 1] = g.y;
-        x[4 * v + 2] = g.z;
-        x[4 * v + 3] = g.w;
+        x[4 * v] = canon(g.x);
+        x[4 * v + 1] = canon(g.y);
+        x[4 * v + 2] = canon(g.z);
+        x[4 * v + 3] = canon(g.w);
       }
     }
   }
@@ -302,7 +330,10 @@ struct Row {
         if (4 * NT * v >= n) break;   // uniform
         const int j0 = 4 * (threadIdx.x + NT * v);
         const float g[4] = {x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
-        if (j0 < n && (!KEPT || j0 + 4 > lo_)) f(g, j0, GroupRange<KEPT>{lo() - j0, n - j0});
+        if ((!KEPT || 4 * NT * v >= lo_) && 4 * NT * (v + 1) <= n)   // uniform
+          f(g, j0, GroupRange<KEPT>{0, 4, true});
+        else if (j0 < n && (!KEPT || j0 + 4 > lo_))
+          f(g, j0, GroupRange<KEPT>{lo() - j0, n - j0, false});
       }
     } else {
       constexpr int kBatch = 4;   // float4 groups in flight per thread
@@ -313,10 +344,41 @@ struct Row {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int j0 = 4 * (v0 + u * NT);
-          const float g[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-          if (j0 < n && (!KEPT || j0 + 4 > lo_)) f(g, j0, GroupRange<KEPT>{lo() - j0, n - j0});
+          const float g[4] = {canon(q[u].x), canon(q[u].y), canon(q[u].z), canon(q[u].w)};
+          if (j0 < n && (!KEPT || j0 + 4 > lo_)) f(g, j0, GroupRange<KEPT>{lo() - j0, n - j0, false});
         }
       }
+    }
+  }
+
+  // Running min / max over the keys in [lo, n) (NaN scores are skipped).
+  __device__ inline void minmax(float& mn, float& mx) const {
+    constexpr float kInf = __builtin_huge_valf();
+    if constexpr (RES) {
+#pragma unroll
+      for (int v = 0; v < R / 4; ++v) {
+        if (4 * NT * v >= n) break;   // uniform
+        const float* g = &x[4 * v];
+        if ((!KEPT || 4 * NT * v >= lo_) && 4 * NT * (v + 1) <= n) {  // uniform: all in range
+          mn = min3_raw(mn, g[0], g[1]);
+          mn = min3_raw(mn, g[2], g[3]);
+          mx = max3_raw(mx, g[0], g[1]);
+          mx = max3_raw(mx, g[2], g[3]);
+        } else {
+          const int j0 = 4 * (threadIdx.x + NT * v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool in = (!KEPT || j0 + e >= lo_) && j0 + e < n;
+            mn = min_raw(mn, in ? g[e] : kInf);
+            mx = max_raw(mx, in ? g[e] : -kInf);
+          }
+        }
+      }
+    } else {
+      each([&](float s, int) {
+        mn = min_raw(mn, s);
+        mx = max_raw(mx, s);
+      });
     }
   }
 
@@ -347,7 +409,7 @@ struct Row {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int j0 = 4 * (v0 + u * NT);
-          const float s[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
+          const float s[4] = {canon(g[u].x), canon(g[u].y), canon(g[u].z), canon(g[u].w)};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if ((!KEPT || j0 + e >= lo_) && j0 + e < n) f(s[e], j0 + e);
@@ -502,7 +564,6 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     for (int e = 0; e < 4; ++e) {
       b[e] = bucket(x[e]);
       c[e] = rng.ok(e) && b[e] >= t;
-      raw[e] = 0;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -711,13 +772,11 @@ void topk_kernel(TopkArgs a, int first) {
   }
   row.load();
   // Clear the histogram while the row loads.
-  for (int w = threadIdx.x; w < (int)(sizeof(sm.cnt) / 4); w += NT) sm.cnt[w] = 0u;
+  for (int w = threadIdx.x; w < (int)(sizeof(sm.cnt) / 16); w += NT)
+    reinterpret_cast<uint4*>(sm.cnt)[w] = make_uint4(0u, 0u, 0u, 0u);
   if (threadIdx.x == 0) sm.s_sel[2] = 0u;
   float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
-  row.each([&](float x, int) {
-    lo = fminf(lo, x);
-    hi = fmaxf(hi, x);
-  });
+  row.minmax(lo, hi);
   block_minmax<NT>(lo, hi, sm.s_red);
   const bool fast = (!W16 || n <= 65535) &&
                     select_by_buckets<NT, R, RES, KEPT, W16, KMAX>(row, lo, hi, K, m, out, sm);
