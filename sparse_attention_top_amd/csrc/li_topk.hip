@@ -65,9 +65,10 @@ constexpr int kBuckets = 4096;        // fast-path histogram
 constexpr int kRadixBins = 2048;      // fallback digit histogram
 constexpr int kSegMax = 64;           // longest bucket segment the rank step takes
 // Zero composites after the candidates (at most k + kSegMax of them): the rank
-// step of a key may read up to
-// kSegMax + 1 slots past the end of its segment (they hold smaller composites
-// of later segments, or these zeros, and never count).
+// step of a key reads its segment two slots at a time up to the longest
+// segment among the keys its thread ranks together, i.e. up to kSegMax + 1
+// slots past the end of its own segment (they hold smaller composites of later
+// segments, or these zeros, and never count).
 constexpr int kBufPad = kSegMax + 4;
 
 // -0 -> +0 (IEEE: -0 + +0 = +0; every other value is unchanged).
@@ -582,51 +583,68 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   __syncthreads();
 
   // Rank every grouped key inside its segment and store it at its sorted
-  // position. Four candidates per thread are ranked together; each step reads
-  // two consecutive slots of each segment. Slots past a segment's end hold
-  // smaller composites (later segments, or the zero pad), so they never count
-  // and need no mask.
-  for (uint32_t p0 = tid; p0 < ncand; p0 += 4 * NT) {
-    unsigned long long me[4];
-    uint32_t s0[4], s1[4], rank[4];
-    int bk[4];
+  // position. NB candidates per thread (slots p0 + u*NT) are ranked together;
+  // each step reads two consecutive slots of each segment. Slots past a
+  // segment's end hold smaller composites (later segments, or the zero pad),
+  // so they never count and need no mask. FULL: every slot is < ncand.
+  auto rank_batch = [&](uint32_t p0, auto nb_tag, auto full_tag) {
+    constexpr int NB = decltype(nb_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;
+    unsigned long long me[NB];
+    uint32_t s0[NB], s1[NB], rank[NB];
+    int bk[NB];
     uint32_t len = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const uint32_t p = p0 + u * NT;
-      me[u] = sm.buf[p < ncand ? p : 0];
+      me[u] = sm.buf[FULL || p < ncand ? p : 0];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NB; ++u) {
       if constexpr (W16) bk[u] = bucket_of(me[u]);
       else bk[u] = bucket(from_ord((uint32_t)(me[u] >> 32)));
       cnt.get_pair(bk[u], s0[u], s1[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (p0 + u * NT >= ncand) s1[u] = s0[u];
+    for (int u = 0; u < NB; ++u) {
+      if (!FULL && p0 + u * NT >= ncand) s1[u] = s0[u];
       rank[u] = 0;
       len = max(len, s1[u] - s0[u]);
     }
+    const unsigned long long* seg[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) seg[u] = &sm.buf[s0[u]];
     for (uint32_t i = 0; i < len; i += 2) {
-      unsigned long long v[4][2];
+      unsigned long long v[NB][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < NB; ++u)
 #pragma unroll
-        for (int w = 0; w < 2; ++w) v[u][w] = sm.buf[s0[u] + i + w];
+        for (int w = 0; w < 2; ++w) v[u][w] = seg[u][w];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < NB; ++u) {
+        seg[u] += 2;
 #pragma unroll
         for (int w = 0; w < 2; ++w) rank[u] += v[u][w] > me[u] ? 1u : 0u;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (s0[u] < s1[u] && !(bk[u] == t && rank[u] >= need)) {
+    for (int u = 0; u < NB; ++u) {
+      if ((FULL || s0[u] < s1[u]) && !(bk[u] == t && rank[u] >= need)) {
         if constexpr (W16) out.put_key(s0[u] + rank[u], bucket_index_of(me[u]), me[u]);
         else out.put(s0[u] + rank[u], me[u]);
       }
     }
-  }
+  };
+  // Whole batches of four slots per thread, then the rest one slot per thread
+  // (the candidate count is often just over a multiple of 4 * NT), skipping
+  // waves that hold no candidate.
+  using std::integral_constant;
+  uint32_t base = 0;
+  for (; base + 4 * NT <= ncand; base += 4 * NT)
+    rank_batch(base + tid, integral_constant<int, 4>{}, integral_constant<bool, true>{});
+  for (; base < ncand; base += NT)
+    if (base + (tid & ~63) < ncand)   // uniform per wave
+      rank_batch(base + tid, integral_constant<int, 1>{}, integral_constant<bool, false>{});
   fill_tail(m, K, out, NT);
   return true;
 }
@@ -726,9 +744,11 @@ __device__ void select_by_radix(const Row<NT, R, RES, KEPT>& row, int K, int m, 
 // W16 (16-bit bucket counters) is used only for rows of at most 65535 keys.
 // A row's latency is a chain of dependent LDS and memory steps, so throughput
 // comes from rows in flight: the 256-thread kernel (every row up to 8K keys, in
-// one launch) is held to the register budget of five workgroups per CU.
+// one launch) is held to the register budget of six workgroups per CU (80
+// VGPRs; its LDS, about 25 KB, fits six in 160 KB; only the radix fallback
+// spills a few registers).
 template <int NT, int R, bool RES, bool KEPT, bool W16, int KMAX>
-__global__ __launch_bounds__(NT, (NT == 256 && KMAX == kMaxKSmall) ? 5 : 1)
+__global__ __launch_bounds__(NT, (NT == 256 && KMAX == kMaxKSmall) ? 6 : 1)
 void topk_kernel(TopkArgs a, int first) {
   __shared__ Smem<NT, W16, KMAX> sm;
   const RowRec rr = a.rows[first + blockIdx.x];
