@@ -481,35 +481,70 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     if constexpr (W16) return h == 0 ? word[q] >> 16 : word[q] & 0xFFFFu;
     else return word[q];
   };
-  if (n <= K) {
-    if (tid == 0) {
-      sm.s_sel[0] = 0u;           // every bucket is taken whole
-      sm.s_sel[1] = 0xFFFFFFFFu;
-    }
-  } else if (act && before < (uint32_t)K && (uint32_t)K <= before + local) {
-    uint32_t cum = before;
+  // After the scan every thread knows how its buckets stand against t (the
+  // bucket holding the K-th largest key) without knowing t: all at or above it
+  // (its run ends before K keys), holding it (the finder), or all below. Rows
+  // of at most K keys take every bucket (t = 0).
+  const bool whole = n <= K;
+  const bool above = act && (whole || before + local < (uint32_t)K);
+  const bool finder = act && !whole && before < (uint32_t)K && (uint32_t)K <= before + local;
+  // The largest count at or above t (a longer segment sends the row to the
+  // radix path: it would exceed buf, or make ranking quadratic).
+  uint32_t big = 0;
+  if (finder) {
+    uint32_t cum = before, t_cum = 0, t_cnt = 0;
+    int tb = 0;
 #pragma unroll
     for (int q = 0; q < WPT; ++q)
 #pragma unroll
       for (int h = 0; h < BPW; ++h) {
         const uint32_t c = count_at(q, h);
         if (cum < (uint32_t)K && (uint32_t)K <= cum + c) {
-          sm.s_sel[0] = (uint32_t)(nb - 1 - (tid * BPT + BPW * q + h));
-          sm.s_sel[1] = (uint32_t)K - cum;
+          tb = nb - 1 - (tid * BPT + BPW * q + h);
+          t_cum = cum;
+          t_cnt = c;
         }
         cum += c;
       }
+    sm.s_sel[0] = (uint32_t)tb;
+    sm.s_sel[1] = (uint32_t)K - t_cum;
+    sm.s_sel[3] = t_cum + t_cnt;   // keys in buckets >= t
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      const int b_hi = nb - 1 - (tid * BPT + BPW * q);
+      if constexpr (W16) {
+        const uint32_t c_hi = count_at(q, 0), c_lo = count_at(q, 1);
+        if (b_hi >= tb && c_hi > big) big = c_hi;
+        if (b_hi - 1 >= tb && c_lo > big) big = c_lo;
+      } else {
+        const uint32_t c = count_at(q, 0);
+        if (b_hi >= tb && c > big) big = c;
+      }
+    }
+  } else if (above) {
+    // two 16-bit fields at a time
+    if constexpr (W16) {
+      uint32_t mx = word[0];
+#pragma unroll
+      for (int q = 1; q < WPT; ++q) mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+          __builtin_bit_cast(u16x2_t, mx), __builtin_bit_cast(u16x2_t, word[q])));
+      big = max(mx >> 16, mx & 0xFFFFu);
+    } else {
+#pragma unroll
+      for (int q = 0; q < WPT; ++q) big = max(big, word[q]);
+    }
   }
-  __syncthreads();
-  const int t = (int)sm.s_sel[0];
-  const uint32_t need = sm.s_sel[1];
-  // Counts become exclusive offsets from the top bucket for the threads that
-  // own buckets >= t (16-bit fields are each written on their own, so a field
-  // that wraps below t cannot spill into its neighbour; only buckets >= t are
-  // used, and their offsets stay below K + kSegMax). Track the largest segment
-  // at or above t.
-  if (act && nb - 1 - tid * BPT >= t) {
-    uint32_t cum = before, big = 0;
+  if (whole && tid == 0) {
+    sm.s_sel[0] = 0u;
+    sm.s_sel[1] = 0xFFFFFFFFu;
+    sm.s_sel[3] = (uint32_t)n;
+  }
+  // Counts become exclusive offsets from the top bucket for the threads whose
+  // buckets reach t (16-bit fields are each written on their own, so a field
+  // that wraps cannot spill into its neighbour; only buckets >= t are used,
+  // and their offsets stay below K + kSegMax).
+  if (above || finder) {
+    uint32_t cum = before;
 #pragma unroll
     for (int q = 0; q < WPT; ++q) {
       if constexpr (W16) {
@@ -521,37 +556,15 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
         cum += count_at(q, 0);
       }
     }
-    if (nb - BPT - tid * BPT >= t) {
-      // every bucket of the thread is at or above t: the largest count, two
-      // 16-bit fields at a time
-      if constexpr (W16) {
-        uint32_t mx = word[0];
-#pragma unroll
-        for (int q = 1; q < WPT; ++q) mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
-            __builtin_bit_cast(u16x2_t, mx), __builtin_bit_cast(u16x2_t, word[q])));
-        big = max(mx >> 16, mx & 0xFFFFu);
-      } else {
-#pragma unroll
-        for (int q = 0; q < WPT; ++q) big = max(big, word[q]);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < WPT; ++q) {
-        const int b_hi = nb - 1 - (tid * BPT + BPW * q);
-        if constexpr (W16) {
-          const uint32_t c_hi = count_at(q, 0), c_lo = count_at(q, 1);
-          if (b_hi >= t && c_hi > big) big = c_hi;
-          if (b_hi - 1 >= t && c_lo > big) big = c_lo;
-        } else {
-          const uint32_t c = count_at(q, 0);
-          if (b_hi >= t && c > big) big = c;
-        }
-      }
-    }
-    if (big > (uint32_t)kSegMax) atomicMax(&sm.s_sel[2], big);
   }
+  if (big > (uint32_t)kSegMax) atomicMax(&sm.s_sel[2], big);
   __syncthreads();
   if (sm.s_sel[2] != 0u) return false;
+  const int t = (int)sm.s_sel[0];
+  const uint32_t need = sm.s_sel[1];
+  const uint32_t ncand = sm.s_sel[3];
+  // Zero composites past the candidates (the counting sort writes [0, ncand)).
+  for (int e = tid; e < kBufPad; e += NT) sm.buf[ncand + e] = 0ull;
 
   // Counting sort of the keys of buckets >= t into their bucket segments.
   // Afterwards bucket b's segment is [end(b+1), end(b)) (end(nb) = 0: the zero
@@ -577,9 +590,6 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
         else sm.buf[pos] = composite(x[e], j0 + e);
       }
   });
-  __syncthreads();
-  const uint32_t ncand = cnt.get(t);
-  for (int e = tid; e < kBufPad; e += NT) sm.buf[ncand + e] = 0ull;
   __syncthreads();
 
   // Rank every grouped key inside its segment and store it at its sorted
