@@ -120,14 +120,13 @@ __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFF
 
 // The fast path's composite for rows of at most 2^20 keys also carries the
 // key's bucket b in the top 12 bits of its low word: (ord(score), b, 2^20-1-j).
-// s is canonical (read through Row).
+// s is canonical (read through Row); rj = 2^20-1-j.
 // Inside a bucket segment the order is the plain composite's (b is common);
 // a key of a lower bucket has a lower score, so its composite is lower whatever
 // its low word holds.
 constexpr uint32_t kIdxMask = (1u << 20) - 1;
-__device__ inline unsigned long long bucket_composite(float s, int b, int j) {
-  return ((unsigned long long)ord_bits(s) << 32) |
-         (unsigned long long)(((uint32_t)b << 20) | (kIdxMask - (uint32_t)j));
+__device__ inline unsigned long long bucket_composite(float s, int b, uint32_t rj) {
+  return ((unsigned long long)ord_bits(s) << 32) | (((uint32_t)b << 20) | rj);
 }
 __device__ inline int bucket_of(unsigned long long c) { return (int)((uint32_t)c >> 20); }
 __device__ inline int32_t bucket_index_of(unsigned long long c) {
@@ -171,6 +170,12 @@ struct Smem {
 static_assert(kBuckets / 2 >= kRadixBins, "radix digits reuse the histogram words");
 
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + (w >> 16) + (w & 0xFFFF) in one instruction (a u16 dot product).
+__device__ inline uint32_t add_halves(uint32_t w, uint32_t acc) {
+  const u16x2_t one = {1, 1};
+  return __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2_t, w), one, acc, false);
+}
 
 template <bool W16>
 struct Counters {
@@ -472,7 +477,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
 #pragma unroll
     for (int q = 0; q < WPT; ++q) {
       word[q] = cnt.word(w_top - q);
-      local += W16 ? (word[q] >> 16) + (word[q] & 0xFFFFu) : word[q];
+      local = W16 ? add_halves(word[q], local) : local + word[q];
     }
   }
   const uint32_t before = block_exclusive_scan<NT>(local, sm.s_wave, nw_act);
@@ -548,9 +553,11 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
 #pragma unroll
     for (int q = 0; q < WPT; ++q) {
       if constexpr (W16) {
-        const uint32_t c_hi = count_at(q, 0), c_lo = count_at(q, 1);
-        cnt.word(w_top - q) = ((cum & 0xFFFFu) << 16) | ((cum + c_hi) & 0xFFFFu);
-        cum += c_hi + c_lo;
+        // (cum, cum + c_hi) as one packed 16-bit add; cum < 2^16 here
+        const u16x2_t pair = __builtin_bit_cast(u16x2_t, (cum << 16) | cum);
+        const u16x2_t hi_lo = __builtin_bit_cast(u16x2_t, word[q] >> 16);   // (0, c_hi)
+        cnt.word(w_top - q) = __builtin_bit_cast(uint32_t, pair + hi_lo);
+        cum = add_halves(word[q], cum);
       } else {
         cnt.word(w_top - q) = cum;
         cum += count_at(q, 0);
@@ -571,6 +578,9 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   // word past the buckets). The four atomics of a group are all issued before
   // their results are read.
   row.each4([&](const float (&x)[4], int j0, auto rng) {
+    // 2^20-1-j for j = j0 + e: j0 is a multiple of 4, so it is the complement
+    // of j0 in 20 bits with its low two bits flipped by e
+    const uint32_t rj0 = ~(uint32_t)j0 & kIdxMask;
     int b[4];
     bool c[4];
     uint32_t raw[4];
@@ -586,8 +596,10 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     for (int e = 0; e < 4; ++e)
       if (c[e]) {
         const uint32_t pos = cnt.field(raw[e], b[e]);
-        if constexpr (W16) sm.buf[pos] = bucket_composite(x[e], b[e], j0 + e);
-        else sm.buf[pos] = composite(x[e], j0 + e);
+        if constexpr (W16)
+          sm.buf[pos] = bucket_composite(x[e], b[e], rj0 ^ (uint32_t)e);
+        else
+          sm.buf[pos] = composite(x[e], j0 + e);
       }
   });
   __syncthreads();
