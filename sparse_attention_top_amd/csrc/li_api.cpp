@@ -340,7 +340,10 @@ li_status li_metadata(const li_problem* p, const li_lengths* L, int32_t num_cus,
       max_sq = std::max(max_sq, sq[b]);
       max_sk = std::max(max_sk, sk[b]);
     }
-    const int variant = max_sq <= 2 ? kVarDecode : (max_sq <= 4 ? kVarMid : kVarPrefill);
+    const bool quant = p->dtype_qk == LI_DTYPE_E4M3FN || p->dtype_qk == LI_DTYPE_I8;
+    const int variant = max_sq <= 2 ? kVarDecode
+                        : max_sq <= 4 ? kVarMid
+                        : quant ? kVarQuant : kVarPrefill;
     const int TQ = kVariantTileQ[variant];
     const int KT = kVariantTileK[variant];
 

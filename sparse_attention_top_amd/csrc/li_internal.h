@@ -29,7 +29,7 @@ namespace li {
 // a second-pass record selects the row's top k among the chunk lists.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMetaMagic = 0x444D494Cu;  // "LIMD"
-constexpr uint32_t kMetaVersion = 7;
+constexpr uint32_t kMetaVersion = 8;
 
 // Top-k size classes: class c holds the rows of at most kTopkClassKeys[c]
 // visible keys (the last class is unbounded) and runs with kTopkClassThreads[c]
@@ -127,18 +127,22 @@ static_assert(sizeof(RowRec) == 32, "row record size");
 // key slices; KT keys staged in LDS per step. Prefill workgroups have 8 waves
 // (one per CU); the short-sequence ones have 4 and run two per CU, so that one
 // workgroup's start (query loads, first stages) overlaps the other's key loop.
+// fp8 / int8 prefill has 4 waves in each of three workgroups per CU (three
+// waves per SIMD: its epilogue, not the matrix cores, bounds it, and the third
+// wave hides the epilogue's wait for the MFMA results).
 enum ScoreVariant : int32_t {
   kVarPrefill = 0,  // WQ=8, WK=1: 8 query rows share each staged key tile
   kVarMid = 1,      // WQ=4, WK=1: 4 query rows
   kVarDecode = 2,   // WQ=2, WK=2: 2 query rows, two waves per row split the keys
+  kVarQuant = 3,    // WQ=4, WK=1: 4 query rows, fp8 / int8 sequences of more than 4 rows
 };
-constexpr int kVariantTileQ[3] = {8, 4, 2};
-constexpr int kVariantWaves[3] = {8, 4, 4};
+constexpr int kVariantTileQ[4] = {8, 4, 2, 4};
+constexpr int kVariantWaves[4] = {8, 4, 4, 4};
 // Keys per staged tile: 256 for prefill (half the stage barriers per MFMA of
 // 128-key tiles, 1.4% faster on a causal 8K prefill although its eight query
 // rows, 128 KB at D = 128, then no longer fit in LDS beside a stage), 128 for
 // the two-per-CU variants, whose LDS holds two stages at most.
-constexpr int kVariantTileK[3] = {256, 128, 128};
+constexpr int kVariantTileK[4] = {256, 128, 128, 128};
 
 // ---------------------------------------------------------------------------
 // Kernel arguments

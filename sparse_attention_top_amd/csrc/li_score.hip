@@ -14,7 +14,8 @@
 //   * WQ rows x WK key slices of waves, two waves per SIMD so that one can issue
 //     while the other waits: 8 waves in one workgroup per CU for prefill tiles,
 //     4 waves in each of two workgroups per CU for short sequences (one
-//     workgroup's start then overlaps the other's key loop); a wave holds its
+//     workgroup's start then overlaps the other's key loop), and for fp8 / int8
+//     prefill 4 waves in each of three workgroups per CU (below); a wave holds its
 //     row's query heads in VGPRs as MFMA A-operands for the whole key loop
 //     (16-bit D = 128 rows arrive through LDS as coalesced blocks, others by
 //     direct loads);
@@ -24,8 +25,15 @@
 //   * per 32-key slice a wave runs NT x (D / k-step) MFMA 32x32 ops with heads on
 //     the M axis and keys on the N axis, with B fragments read one slice ahead;
 //     each lane then holds 16 heads of one key per tile, applies ReLU and the
-//     per-head weight (interleaved with the next slice's MFMAs), and one
-//     cross-lane swap-add over the two half-waves completes the reduction;
+//     per-head weight (interleaved with the next slice's MFMAs: two accumulator
+//     sets, PP), and one cross-lane swap-add over the two half-waves completes
+//     the reduction. fp8 / int8 MFMAs cover a slice in a quarter of the bf16
+//     count, so there the epilogue's two VALU operations per (head, key) bound
+//     the kernel; that variant keeps one accumulator set (PP = false: a slice's
+//     epilogue runs before the next slice's MFMAs), which brings it to 168
+//     VGPRs and three waves per SIMD, and the waves hide each other's wait for
+//     MFMA results (5.53 -> 5.27 ms on a 16-sequence fp8 prefill, identical
+//     outputs; on 4-row fp8 decode it was 6% slower, so kVarMid keeps PP);
 //   * with key blocks (block_len > 1) the maximum over each block's visible keys
 //     is taken across lanes before the store, so one float per block leaves.
 #include "li_internal.h"
@@ -173,8 +181,9 @@ template <int N> __device__ inline void stage_barrier() {
 
 // BL: store one score per block of block_len keys (the block maximum) instead
 // of one per key.
-template <int DT, int D, int NT, int WQ, int WK, int KT, bool BL>
-__global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kernel(ScoreArgs a) {
+template <int DT, int D, int NT, int WQ, int WK, int KT, bool BL, bool PP = true,
+          int MINB = (WQ * WK == 4 ? 2 : 1)>
+__global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) {
   using M = Mma<DT>;
   using Frag = typename M::Frag;
   using Acc = typename M::Acc;
@@ -489,6 +498,29 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
     const int nbase = frag_base(nbuf, nsub);
     if (QUANT) ksn = ksc[nbuf][nsub * 32 + col];
     float p0 = 0.f, p1 = 0.f;
+    if constexpr (!PP) {
+      // One accumulator set (old aliases acc): the previous slice's epilogue
+      // first, in the same order as below, then this slice's MFMAs.
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int u = 0; u < EPM; u += 2) {
+            const int e = s * EPM + u;
+            p0 = fmaf(wr[t][e], M::relu(old[t], e), p0);
+            p1 = fmaf(wr[t][e + 1], M::relu(old[t], e + 1), p1);
+          }
+      asm volatile("" : "+v"(p0), "+v"(p1));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = M::mma(qf[t][s], bf[s], s == 0 ? M::zero() : acc[t]);
+        bf[s] = read_frag(nbase, s);
+      }
+      return p0 + p1;
+    }
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
@@ -568,9 +600,14 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rsrc, off, 0, 0);
   };
 
-  Acc acc0[NT], acc1[NT];   // even slices of a stage accumulate in acc0, odd in acc1
+  // PP: even slices of a stage accumulate in acc0, odd ones in acc1; else all
+  // in acc0. The first slice's (dropped) epilogue reads zeros.
+  Acc acc0[NT], acc1[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc1[t] = M::zero();   // read by slice 0's (dropped) epilogue
+  for (int t = 0; t < NT; ++t) {
+    acc1[t] = M::zero();
+    if (!PP) acc0[t] = M::zero();
+  }
   float ks0 = 1.f, ks1 = 1.f;
   float hp = 0.f, hks = 1.f;   // an even slice's part, finished with the next one
   int hkb = 0;
@@ -590,17 +627,17 @@ __global__ __launch_bounds__(WQ * WK * 64, WQ * WK == 4 ? 2 : 1) void score_kern
       // previous slice: (st, i-1), or the last slice of stage st-1
       const int pkb = i > 0 ? slice_key(st, i - 1) : slice_key(st - 1, SPS - 1);
       if (i % 2 == 0) {
-        hp = step(st, ic, acc0, acc1, ks0);
+        hp = PP ? step(st, ic, acc0, acc1, ks0) : step(st, ic, acc0, acc0, ks0);
         hkb = pkb;
         hks = ks1;
         hvalid = i > 0 || st > 0;
       } else {
-        const float part = step(st, ic, acc1, acc0, ks1);
+        const float part = PP ? step(st, ic, acc1, acc0, ks1) : step(st, ic, acc0, acc0, ks1);
         finish2(hp, hkb, hks, hvalid, part, pkb, ks0);
       }
     });
   }
-  finish(epi(acc1), slice_key(nstages - 1, SPS - 1), ks1, true);
+  finish(epi(PP ? acc1 : acc0), slice_key(nstages - 1, SPS - 1), ks1, true);
 }
 
 template <int DT, int D, int NT, bool BL>
@@ -618,6 +655,14 @@ hipError_t launch_v(int variant, int num_items, const ScoreArgs& a, hipStream_t 
       hipLaunchKernelGGL((score_kernel<DT, D, NT, 2, 2, kVariantTileK[kVarDecode], BL>),
                          dim3(num_items), dim3(64 * kVariantWaves[kVarDecode]), 0, s, a);
       break;
+    case kVarQuant:
+      if constexpr (DT == LI_DTYPE_E4M3FN || DT == LI_DTYPE_I8) {
+        hipLaunchKernelGGL((score_kernel<DT, D, NT, 4, 1, kVariantTileK[kVarQuant], BL, false, 3>),
+                           dim3(num_items), dim3(64 * kVariantWaves[kVarQuant]), 0, s, a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
     default:
       return hipErrorInvalidValue;
   }
