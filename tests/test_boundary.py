@@ -389,6 +389,20 @@ def test_split_decision(lib, case, cus, splits):
         assert int(h["cand_idx_off"]) > int(h["cand_val_off"]) > 0
 
 
+@pytest.mark.parametrize("dtype,s1,variant,tile_q", [
+    ("bf16", 2, 2, 2), ("bf16", 4, 1, 4), ("bf16", 64, 0, 8),
+    ("e4m3fn", 2, 2, 2), ("e4m3fn", 4, 1, 4), ("e4m3fn", 64, 3, 4), ("i8", 5, 3, 4)])
+def test_metadata_score_variant(lib, dtype, s1, variant, tile_q):
+    """Decode (<= 2 query rows) and 3-4-row problems keep their variants whatever
+    the dtype; longer fp8 / int8 sequences take the three-waves-per-SIMD variant
+    of 4-row tiles, 16-bit ones the 8-row prefill tiles."""
+    p = B.make_problem(layout_q="BSND", layout_k="BSND", dtype_qk=dtype, dtype_w="f32",
+                       batch=2, s1=s1, s2=1024, n1=64, d=128, sparse_count=64, sparse_mode=0)
+    h, _, items = B.parse_metadata(B.li_metadata(p, B.make_lengths()))
+    assert int(h["variant"]) == variant and int(h["tile_q"]) == tile_q
+    assert all(int(it["q0"]) % tile_q == 0 for it in items)
+
+
 def test_metadata_heaviest_first_and_balanced(lib):
     p = B.make_problem(layout_q="BSND", layout_k="BSND", dtype_qk="bf16", dtype_w="bf16",
                        batch=1, s1=8192, s2=8192, n1=64, d=128, sparse_count=2048, sparse_mode=3)
