@@ -561,13 +561,14 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   // Cross-half swap-add (both halves end up with the full sum over heads) and
   // the store of the slice starting at key kb by the lower half-wave; keys at
   // or past the row's limit fall outside the buffer record and are dropped.
+  // Stored scores are canonical (x + 0: -0 becomes +0), which the top-k relies on.
   // With blocks, keys past the limit count as -inf in their block's maximum
   // and the first lane of each block stores it.
   auto finish = [&](float part, int kb, float ks, bool valid) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
                                                      __float_as_uint(part), false, false);
     float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (QUANT) tot *= ks;
+    tot = QUANT ? fmaf(tot, ks, 0.0f) : tot + 0.0f;   // canonical: never -0
     int off;
     if constexpr (BL) {
       const int j = kb + col;
@@ -586,7 +587,7 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb),
                                                      false, false);
     float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (QUANT) tot *= half ? ksb : ksa;
+    tot = QUANT ? fmaf(tot, half ? ksb : ksa, 0.0f) : tot + 0.0f;   // canonical: never -0
     const int kb = half ? kbb : kba;
     const bool valid = half ? true : valida;
     int off;

@@ -30,8 +30,8 @@
 //   5. each such key's rank inside its segment (a count of larger composites)
 //      gives its final sorted position, where it is stored; keys of bucket t
 //      ranked past what is still needed are dropped.
-// Scores are canonicalised as they are read (x + 0: -0 becomes +0, and min /
-// max then need no NaN quieting).
+// Scores arrive canonical: the score kernel stores x + 0 (no -0, NaNs quiet),
+// so composites need no folding of -0 and min / max no NaN quieting.
 // Fallback (zero or non-finite range, or a bucket >= t holding more than
 // kSegMax keys, e.g. many equal scores): MSD radix select over the composite
 // with 11/11/10-bit digits (score first, index digits only on ties at the
@@ -76,7 +76,7 @@ __device__ inline float canon(float x) { return x + 0.0f; }
 
 // min / max as single instructions. The compiler's fminf / fmaxf first quiet
 // signalling NaNs in every operand it cannot prove canonical (one more
-// instruction per operand); scores here are canonical already (read as x + 0).
+// instruction per operand); the scores are canonical already (stored as x + 0).
 __device__ inline float min_raw(float a, float b) {
   float r;
   asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -120,7 +120,7 @@ __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFF
 
 // The fast path's composite for rows of at most 2^20 keys also carries the
 // key's bucket b in the top 12 bits of its low word: (ord(score), b, 2^20-1-j).
-// s is canonical (read through Row); rj = 2^20-1-j.
+// s is canonical (as the score kernel stores it); rj = 2^20-1-j.
 // Inside a bucket segment the order is the plain composite's (b is common);
 // a key of a lower bucket has a lower score, so its composite is lower whatever
 // its low word holds.
@@ -318,10 +318,10 @@ struct Row {
       for (int v = 0; v < R / 4; ++v) {
         if (4 * NT * v >= n) break;   // uniform
         const float4 g = group(threadIdx.x + NT * v);
-        x[4 * v] = canon(g.x);
-        x[4 * v + 1] = canon(g.y);
-        x[4 * v + 2] = canon(g.z);
-        x[4 * v + 3] = canon(g.w);
+        x[4 * v] = g.x;
+        x[4 * v + 1] = g.y;
+        x[4 * v + 2] = g.z;
+        x[4 * v + 3] = g.w;
       }
     }
   }
@@ -350,7 +350,7 @@ struct Row {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int j0 = 4 * (v0 + u * NT);
-          const float g[4] = {canon(q[u].x), canon(q[u].y), canon(q[u].z), canon(q[u].w)};
+          const float g[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
           if (j0 < n && (!KEPT || j0 + 4 > lo_)) f(g, j0, GroupRange<KEPT>{lo() - j0, n - j0, false});
         }
       }
@@ -415,7 +415,7 @@ struct Row {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int j0 = 4 * (v0 + u * NT);
-          const float s[4] = {canon(g[u].x), canon(g[u].y), canon(g[u].z), canon(g[u].w)};
+          const float s[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if ((!KEPT || j0 + e >= lo_) && j0 + e < n) f(s[e], j0 + e);
@@ -497,35 +497,47 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   // radix path: it would exceed buf, or make ranking quadratic).
   uint32_t big = 0;
   if (finder) {
-    uint32_t cum = before, t_cum = 0, t_cnt = 0;
-    int tb = 0;
+    // The word holding bucket t is the first whose running total reaches K:
+    // one pass over the words, selecting without branches; the largest count
+    // of the words before it folds in on the way (every bucket there is > t).
+    uint32_t cum = before, sel_w = 0, sel_cum = 0, mx = 0;
+    int sel_q = 0;
+    bool found = false;
 #pragma unroll
-    for (int q = 0; q < WPT; ++q)
-#pragma unroll
-      for (int h = 0; h < BPW; ++h) {
-        const uint32_t c = count_at(q, h);
-        if (cum < (uint32_t)K && (uint32_t)K <= cum + c) {
-          tb = nb - 1 - (tid * BPT + BPW * q + h);
-          t_cum = cum;
-          t_cnt = c;
-        }
-        cum += c;
+    for (int q = 0; q < WPT; ++q) {
+      const uint32_t nxt = W16 ? add_halves(word[q], cum) : cum + word[q];
+      const bool take = !found && (uint32_t)K <= nxt;
+      sel_w = take ? word[q] : sel_w;
+      sel_cum = take ? cum : sel_cum;
+      sel_q = take ? q : sel_q;
+      if constexpr (W16) {
+        const uint32_t wm = found || take ? 0u : word[q];
+        mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+            __builtin_bit_cast(u16x2_t, mx), __builtin_bit_cast(u16x2_t, wm)));
+      } else {
+        mx = found || take ? mx : max(mx, word[q]);
       }
+      found = found || take;
+      cum = nxt;
+    }
+    int tb;
+    uint32_t t_cum, t_cnt;
+    if constexpr (W16) {
+      const uint32_t c_hi = sel_w >> 16, c_lo = sel_w & 0xFFFFu;
+      const bool in_hi = (uint32_t)K <= sel_cum + c_hi;   // t is the word's higher bucket
+      tb = nb - 1 - (tid * BPT + BPW * sel_q + (in_hi ? 0 : 1));
+      t_cum = in_hi ? sel_cum : sel_cum + c_hi;
+      t_cnt = in_hi ? c_hi : c_lo;
+      big = max(max(mx >> 16, mx & 0xFFFFu), max(c_hi, in_hi ? 0u : c_lo));
+    } else {
+      tb = nb - 1 - (tid * BPT + sel_q);
+      t_cum = sel_cum;
+      t_cnt = sel_w;
+      big = max(mx, sel_w);
+    }
     sm.s_sel[0] = (uint32_t)tb;
     sm.s_sel[1] = (uint32_t)K - t_cum;
     sm.s_sel[3] = t_cum + t_cnt;   // keys in buckets >= t
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      const int b_hi = nb - 1 - (tid * BPT + BPW * q);
-      if constexpr (W16) {
-        const uint32_t c_hi = count_at(q, 0), c_lo = count_at(q, 1);
-        if (b_hi >= tb && c_hi > big) big = c_hi;
-        if (b_hi - 1 >= tb && c_lo > big) big = c_lo;
-      } else {
-        const uint32_t c = count_at(q, 0);
-        if (b_hi >= tb && c > big) big = c;
-      }
-    }
   } else if (above) {
     // two 16-bit fields at a time
     if constexpr (W16) {
