@@ -28,8 +28,8 @@
 //   4. every key in a bucket >= t is written to its bucket's segment in LDS
 //      (a counting sort by bucket);
 //   5. each such key's rank inside its segment (a count of larger composites)
-//      gives its final sorted position, where it is stored; keys of bucket t
-//      ranked past what is still needed are dropped.
+//      gives its final sorted position, where it is stored if below k (only
+//      keys of bucket t can land at k or past it).
 // Scores arrive canonical: the score kernel stores x + 0 (no -0, NaNs quiet),
 // so composites need no folding of -0 and min / max no NaN quieting.
 // Fallback (zero or non-finite range, or a bucket >= t holding more than
@@ -119,18 +119,18 @@ __device__ inline unsigned long long composite(float s, int j) {
 __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFFFFFFFFu - (uint32_t)c); }
 
 // The fast path's composite for rows of at most 2^20 keys also carries the
-// key's bucket b in the top 12 bits of its low word: (ord(score), b, 2^20-1-j).
-// s is canonical (as the score kernel stores it); rj = 2^20-1-j.
+// key's bucket b in the low 12 bits of its low word: (ord(score), 2^20-1-j, b).
+// s is canonical (as the score kernel stores it); rjs = (2^20-1-j) << 12.
 // Inside a bucket segment the order is the plain composite's (b is common);
 // a key of a lower bucket has a lower score, so its composite is lower whatever
 // its low word holds.
 constexpr uint32_t kIdxMask = (1u << 20) - 1;
-__device__ inline unsigned long long bucket_composite(float s, int b, uint32_t rj) {
-  return ((unsigned long long)ord_bits(s) << 32) | (((uint32_t)b << 20) | rj);
+__device__ inline unsigned long long bucket_composite(float s, int b, uint32_t rjs) {
+  return ((unsigned long long)ord_bits(s) << 32) | (rjs + (uint32_t)b);
 }
-__device__ inline int bucket_of(unsigned long long c) { return (int)((uint32_t)c >> 20); }
+__device__ inline int bucket_of(unsigned long long c) { return (int)((uint32_t)c & 0xFFFu); }
 __device__ inline int32_t bucket_index_of(unsigned long long c) {
-  return (int32_t)(kIdxMask - ((uint32_t)c & kIdxMask));
+  return (int32_t)(kIdxMask - ((uint32_t)c >> 12));
 }
 
 // Where a record's result goes: output slots idx[d] / val[d] (val may be null).
@@ -164,7 +164,7 @@ struct Smem {
   alignas(16) uint32_t cnt[kCounterWords<W16> + 4];
   unsigned long long buf[KMAX + kSegMax + kBufPad];  // composites grouped by bucket
   uint32_t s_wave[NT / 64];
-  float s_red[2 * (NT / 64)];
+  uint32_t s_red[2 * (NT / 64)];
   uint32_t s_sel[4];
 };
 static_assert(kBuckets / 2 >= kRadixBins, "radix digits reuse the histogram words");
@@ -188,10 +188,12 @@ struct Counters {
   // (get(b + 1), get(b)) from the two adjacent words that hold them.
   __device__ void get_pair(int b, uint32_t& up, uint32_t& at) const {
     if constexpr (W16) {
+      // (w1:w0) >> (16 * (b & 1)) holds (get(b + 1), get(b)) in its low word;
+      // v_alignbit_b32 reads only the low five bits of b << 4
       const uint32_t w0 = word(b >> 1), w1 = word((b >> 1) + 1);
-      const bool odd = (b & 1) != 0;
-      at = odd ? w0 >> 16 : w0 & 0xFFFFu;
-      up = odd ? w1 & 0xFFFFu : w0 >> 16;
+      const uint32_t pair = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)b << 4);
+      at = pair & 0xFFFFu;
+      up = pair >> 16;
     } else {
       at = word(b);
       up = word(b + 1);
@@ -203,12 +205,15 @@ struct Counters {
   }
   // fetch_add split in two, so that several atomics can be in flight before the
   // first result is used: the raw old word, then the bucket's old count in it.
+  template <uint32_t U = 1>
   __device__ uint32_t fetch_add_raw(int b) const {
-    if constexpr (W16) return atomicAdd(&word(b >> 1), 1u << ((b & 1) << 4));
-    else return atomicAdd(&word(b), 1u);
+    if constexpr (W16) return atomicAdd(&word(b >> 1), U << ((b & 1) << 4));
+    else return atomicAdd(&word(b), U);
   }
   __device__ uint32_t field(uint32_t raw, int b) const {
-    if constexpr (W16) return (raw >> ((b & 1) << 4)) & 0xFFFFu;
+    // the field's offset is (b & 1) * 16: v_bfe_u32 reads only the low five
+    // bits of b << 4
+    if constexpr (W16) return __builtin_amdgcn_ubfe(raw, (uint32_t)b << 4, 16);
     else return raw;
   }
 };
@@ -254,23 +259,28 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, in
 }
 
 template <int NT>
-__device__ inline void block_minmax(float& lo, float& hi, float* s_red) {
+__device__ inline void block_minmax(float& lo, float& hi, uint32_t* s_red) {
+  // On order-preserving bits the two reductions are unsigned maxima (of ~ord(lo)
+  // and of ord(hi)) with identity 0, so each DPP step is one fused instruction.
   constexpr int NW = NT / 64;
-  lo = wave_scan(lo, __builtin_huge_valf(), [](float a, float b) { return min_raw(a, b); });
-  hi = wave_scan(hi, -__builtin_huge_valf(), [](float a, float b) { return max_raw(a, b); });
+  const auto umax = [](uint32_t a, uint32_t b) { return max(a, b); };
+  uint32_t a = wave_scan(~ord_bits(lo), 0u, umax);
+  uint32_t b = wave_scan(ord_bits(hi), 0u, umax);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 63) {
-    s_red[wave] = lo;
-    s_red[NW + wave] = hi;
+    s_red[wave] = a;
+    s_red[NW + wave] = b;
   }
   __syncthreads();
-  lo = s_red[0];
-  hi = s_red[NW];
+  a = s_red[0];
+  b = s_red[NW];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
-    lo = min_raw(lo, s_red[w]);
-    hi = max_raw(hi, s_red[NW + w]);
+    a = max(a, s_red[w]);
+    b = max(b, s_red[NW + w]);
   }
+  lo = from_ord(~a);
+  hi = from_ord(b);
 }
 
 // Monotone map of [lo, hi] onto bucket indices 0..nb-1: floor((x - lo) * scale)
@@ -458,6 +468,13 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   if (!(scale <= 3.0e38f)) return false;
   const Bucketing bucket{scale, lo};
   const Counters<W16> cnt{sm.cnt};
+  // Offsets count bytes of buf (U = 8) where (K + kSegMax) * 8 fits a 16-bit
+  // field; the counting sort and the rank step then address buf without a shift.
+  constexpr uint32_t U = (!W16 || KMAX <= 2048) ? 8u : 1u;
+  static_assert(!W16 || U == 1 || (KMAX + kSegMax) * 8 < 65536, "16-bit byte offsets");
+  auto at = [&](uint32_t off) -> unsigned long long& {
+    return *reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(sm.buf) + off * (8 / U));
+  };
 
   row.each([&](float x, int) { cnt.add(bucket(x)); });
   __syncthreads();
@@ -536,7 +553,6 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
       big = max(mx, sel_w);
     }
     sm.s_sel[0] = (uint32_t)tb;
-    sm.s_sel[1] = (uint32_t)K - t_cum;
     sm.s_sel[3] = t_cum + t_cnt;   // keys in buckets >= t
   } else if (above) {
     // two 16-bit fields at a time
@@ -553,26 +569,24 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   }
   if (whole && tid == 0) {
     sm.s_sel[0] = 0u;
-    sm.s_sel[1] = 0xFFFFFFFFu;
     sm.s_sel[3] = (uint32_t)n;
   }
-  // Counts become exclusive offsets from the top bucket for the threads whose
-  // buckets reach t (16-bit fields are each written on their own, so a field
-  // that wraps cannot spill into its neighbour; only buckets >= t are used,
-  // and their offsets stay below K + kSegMax).
+  // Counts become exclusive offsets from the top bucket, in units of U (bytes
+  // of buf where they fit 16 bits), for the threads whose buckets reach t.
+  // Only buckets >= t are used: their offsets stay below (K + kSegMax) * U and
+  // the higher bucket of such a word holds at most kSegMax keys, so the low
+  // field's sum cannot carry into the high one; in words wholly below t it may.
   if (above || finder) {
-    uint32_t cum = before;
+    uint32_t cum = before * U;
 #pragma unroll
     for (int q = 0; q < WPT; ++q) {
       if constexpr (W16) {
-        // (cum, cum + c_hi) as one packed 16-bit add; cum < 2^16 here
-        const u16x2_t pair = __builtin_bit_cast(u16x2_t, (cum << 16) | cum);
-        const u16x2_t hi_lo = __builtin_bit_cast(u16x2_t, word[q] >> 16);   // (0, c_hi)
-        cnt.word(w_top - q) = __builtin_bit_cast(uint32_t, pair + hi_lo);
-        cum = add_halves(word[q], cum);
+        // (cum, cum + c_hi * U) in the (high, low) fields
+        cnt.word(w_top - q) = ((cum << 16) | cum) + (word[q] >> 16) * U;
+        cum = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2_t, word[q]), u16x2_t{U, U}, cum, false);
       } else {
         cnt.word(w_top - q) = cum;
-        cum += count_at(q, 0);
+        cum += count_at(q, 0) * U;
       }
     }
   }
@@ -580,19 +594,21 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   __syncthreads();
   if (sm.s_sel[2] != 0u) return false;
   const int t = (int)sm.s_sel[0];
-  const uint32_t need = sm.s_sel[1];
   const uint32_t ncand = sm.s_sel[3];
   // Zero composites past the candidates (the counting sort writes [0, ncand)).
   for (int e = tid; e < kBufPad; e += NT) sm.buf[ncand + e] = 0ull;
 
+  // (2^20-1-4*tid) << 12: key j = 4*tid + c of this thread has low word
+  // rjt - (c << 12) + b, one three-operand add (the empty asm keeps the base
+  // in a register instead of being recomputed for every key).
+  uint32_t rjt = (kIdxMask - 4u * (uint32_t)tid) << 12;
+  asm volatile("" : "+v"(rjt));
   // Counting sort of the keys of buckets >= t into their bucket segments.
   // Afterwards bucket b's segment is [end(b+1), end(b)) (end(nb) = 0: the zero
   // word past the buckets). The four atomics of a group are all issued before
   // their results are read.
   row.each4([&](const float (&x)[4], int j0, auto rng) {
-    // 2^20-1-j for j = j0 + e: j0 is a multiple of 4, so it is the complement
-    // of j0 in 20 bits with its low two bits flipped by e
-    const uint32_t rj0 = ~(uint32_t)j0 & kIdxMask;
+    const uint32_t rjs0 = rjt - (((uint32_t)j0 - 4u * (uint32_t)tid) << 12);
     int b[4];
     bool c[4];
     uint32_t raw[4];
@@ -603,15 +619,15 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (c[e]) raw[e] = cnt.fetch_add_raw(b[e]);
+      if (c[e]) raw[e] = cnt.template fetch_add_raw<U>(b[e]);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (c[e]) {
         const uint32_t pos = cnt.field(raw[e], b[e]);
         if constexpr (W16)
-          sm.buf[pos] = bucket_composite(x[e], b[e], rj0 ^ (uint32_t)e);
+          at(pos) = bucket_composite(x[e], b[e], rjs0 - ((uint32_t)e << 12));
         else
-          sm.buf[pos] = composite(x[e], j0 + e);
+          at(pos) = composite(x[e], j0 + e);
       }
   });
   __syncthreads();
@@ -647,8 +663,8 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     }
     const unsigned long long* seg[NB];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) seg[u] = &sm.buf[s0[u]];
-    for (uint32_t i = 0; i < len; i += 2) {
+    for (int u = 0; u < NB; ++u) seg[u] = &at(s0[u]);
+    for (uint32_t i = 0; i < len; i += 2 * U) {
       unsigned long long v[NB][2];
 #pragma unroll
       for (int u = 0; u < NB; ++u)
@@ -663,9 +679,12 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     }
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      if ((FULL || s0[u] < s1[u]) && !(bk[u] == t && rank[u] >= need)) {
-        if constexpr (W16) out.put_key(s0[u] + rank[u], bucket_index_of(me[u]), me[u]);
-        else out.put(s0[u] + rank[u], me[u]);
+      // Buckets above t end at or before the K-th slot; bucket t's segment
+      // starts below it, so "slot < K" keeps exactly its first need keys.
+      const uint32_t slot = s0[u] / U + rank[u];
+      if ((FULL || s0[u] < s1[u]) && slot < (uint32_t)K) {
+        if constexpr (W16) out.put_key(slot, bucket_index_of(me[u]), me[u]);
+        else out.put(slot, me[u]);
       }
     }
   };
