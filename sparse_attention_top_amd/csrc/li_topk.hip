@@ -146,6 +146,15 @@ struct Out {
     idx[d] = (gather ? gather[j] : j) + off;
     if (val) val[d] = from_ord((uint32_t)(c >> 32));
   }
+  // Fast-path store from the complemented index r = 2^20-1-j (the composite's
+  // low word >> 12): j + off is one subtraction from a uniform constant, and
+  // both stores take the same 32-bit byte offset from their base.
+  __device__ void put_rj(uint32_t d, uint32_t r, unsigned long long c) const {
+    const uint32_t b = d * 4u;
+    const int32_t v = gather ? gather[kIdxMask - r] + off : (int32_t)((kIdxMask + (uint32_t)off) - r);
+    *reinterpret_cast<int32_t*>(reinterpret_cast<char*>(idx) + b) = v;
+    if (val) *reinterpret_cast<float*>(reinterpret_cast<char*>(val) + b) = from_ord((uint32_t)(c >> 32));
+  }
 };
 
 // W16: bucket counters are 16-bit halves of 32-bit words (rows of at most 65535
@@ -664,7 +673,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     const unsigned long long* seg[NB];
 #pragma unroll
     for (int u = 0; u < NB; ++u) seg[u] = &at(s0[u]);
-    for (uint32_t i = 0; i < len; i += 2 * U) {
+    auto rank_step = [&]() {
       unsigned long long v[NB][2];
 #pragma unroll
       for (int u = 0; u < NB; ++u)
@@ -676,6 +685,14 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
 #pragma unroll
         for (int w = 0; w < 2; ++w) rank[u] += v[u][w] > me[u] ? 1u : 0u;
       }
+    };
+    if constexpr (FULL) {
+      // every slot holds a candidate, whose segment holds at least itself
+      uint32_t i = 0;
+      do rank_step();
+      while ((i += 2 * U) < len);
+    } else {
+      for (uint32_t i = 0; i < len; i += 2 * U) rank_step();
     }
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
@@ -683,7 +700,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
       // starts below it, so "slot < K" keeps exactly its first need keys.
       const uint32_t slot = s0[u] / U + rank[u];
       if ((FULL || s0[u] < s1[u]) && slot < (uint32_t)K) {
-        if constexpr (W16) out.put_key(slot, bucket_index_of(me[u]), me[u]);
+        if constexpr (W16) out.put_rj(slot, (uint32_t)me[u] >> 12, me[u]);
         else out.put(slot, me[u]);
       }
     }
