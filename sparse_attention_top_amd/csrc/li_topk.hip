@@ -151,7 +151,14 @@ struct Out {
   // both stores take the same 32-bit byte offset from their base.
   __device__ void put_rj(uint32_t d, uint32_t r, unsigned long long c) const {
     const uint32_t b = d * 4u;
-    const int32_t v = gather ? gather[kIdxMask - r] + off : (int32_t)((kIdxMask + (uint32_t)off) - r);
+    int32_t v;
+    if (gather) {
+      v = gather[kIdxMask - r] + off;
+    } else {
+      // kept as one subtraction (the compiler would otherwise share the
+      // gather branch's 2^20-1-r and add off to it)
+      asm("v_sub_u32 %0, %1, %2" : "=v"(v) : "s"(kIdxMask + (uint32_t)off), "v"(r));
+    }
     *reinterpret_cast<int32_t*>(reinterpret_cast<char*>(idx) + b) = v;
     if (val) *reinterpret_cast<float*>(reinterpret_cast<char*>(val) + b) = from_ord((uint32_t)(c >> 32));
   }
@@ -664,10 +671,11 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
       else bk[u] = bucket(from_ord((uint32_t)(me[u] >> 32)));
       cnt.get_pair(bk[u], s0[u], s1[u]);
     }
+    // rank[u] starts at the segment's first slot, so it ends as the sorted slot
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       if (!FULL && p0 + u * NT >= ncand) s1[u] = s0[u];
-      rank[u] = 0;
+      rank[u] = s0[u] / U;
       len = max(len, s1[u] - s0[u]);
     }
     const unsigned long long* seg[NB];
@@ -698,7 +706,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     for (int u = 0; u < NB; ++u) {
       // Buckets above t end at or before the K-th slot; bucket t's segment
       // starts below it, so "slot < K" keeps exactly its first need keys.
-      const uint32_t slot = s0[u] / U + rank[u];
+      const uint32_t slot = rank[u];
       if ((FULL || s0[u] < s1[u]) && slot < (uint32_t)K) {
         if constexpr (W16) out.put_rj(slot, (uint32_t)me[u] >> 12, me[u]);
         else out.put(slot, me[u]);
