@@ -144,6 +144,11 @@ constexpr int kVariantWaves[4] = {8, 4, 4, 4};
 // the two-per-CU variants, whose LDS holds two stages at most.
 constexpr int kVariantTileK[4] = {256, 128, 128, 128};
 
+// Buffer resource word 3 for raw (untyped) buffer access on gfx9-family GPUs.
+// With a zero stride, a lane whose byte offset is >= the record count reads 0
+// and has its store dropped by the hardware: masked stores need no branch.
+constexpr int kRsrcWord3 = 0x00020000;
+
 // ---------------------------------------------------------------------------
 // Kernel arguments
 // ---------------------------------------------------------------------------

@@ -131,10 +131,7 @@ __device__ inline float load_weight(const void* w, int dtype, int64_t i) {
   return (float)__builtin_bit_cast(_Float16, bits);
 }
 
-// Buffer resource word 3 for raw (untyped) buffer access on gfx9-family GPUs.
-// With a zero stride, a lane whose byte offset is >= the record count reads 0
-// and has its store dropped by the hardware: masked stores need no branch.
-constexpr int kRsrcWord3 = 0x00020000;
+// Byte offset past any record count: the store is dropped (kRsrcWord3).
 constexpr int kDropOffset = (int)0x80000000u;
 
 template <int N, typename F, int... I>

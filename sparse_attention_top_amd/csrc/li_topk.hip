@@ -147,20 +147,19 @@ struct Out {
     if (val) val[d] = from_ord((uint32_t)(c >> 32));
   }
   // Fast-path store from the complemented index r = 2^20-1-j (the composite's
-  // low word >> 12): j + off is one subtraction from a uniform constant, and
-  // both stores take the same 32-bit byte offset from their base.
-  __device__ void put_rj(uint32_t d, uint32_t r, unsigned long long c) const {
-    const uint32_t b = d * 4u;
+  // low word >> 12) through buffer records of k slots: a slot at or past k is
+  // dropped by the hardware, and j + off is one subtraction from a uniform
+  // constant (records without gather only).
+  __device__ void put_rj(__amdgpu_buffer_rsrc_t ridx, __amdgpu_buffer_rsrc_t rval, uint32_t d,
+                         uint32_t r, unsigned long long c) const {
     int32_t v;
-    if (gather) {
-      v = gather[kIdxMask - r] + off;
-    } else {
-      // kept as one subtraction (the compiler would otherwise share the
-      // gather branch's 2^20-1-r and add off to it)
-      asm("v_sub_u32 %0, %1, %2" : "=v"(v) : "s"(kIdxMask + (uint32_t)off), "v"(r));
-    }
-    *reinterpret_cast<int32_t*>(reinterpret_cast<char*>(idx) + b) = v;
-    if (val) *reinterpret_cast<float*>(reinterpret_cast<char*>(val) + b) = from_ord((uint32_t)(c >> 32));
+    // kept as one subtraction (the compiler would otherwise form 2^20-1-r and
+    // add off to it)
+    asm("v_sub_u32 %0, %1, %2" : "=v"(v) : "s"(kIdxMask + (uint32_t)off), "v"(r));
+    const int b = (int)(d * 4u);
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, ridx, b, 0, 0);
+    if (val) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(from_ord((uint32_t)(c >> 32))), rval, b,
+                                                   0, 0);
   }
 };
 
@@ -648,6 +647,10 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   });
   __syncthreads();
 
+  // Output records of k slots: stores at slot k or past it are dropped.
+  const bool direct = out.gather == nullptr;   // uniform
+  const auto ridx = __builtin_amdgcn_make_buffer_rsrc(out.idx, (short)0, K * 4, kRsrcWord3);
+  const auto rval = __builtin_amdgcn_make_buffer_rsrc(out.val, (short)0, out.val ? K * 4 : 0, kRsrcWord3);
   // Rank every grouped key inside its segment and store it at its sorted
   // position. NB candidates per thread (slots p0 + u*NT) are ranked together;
   // each step reads two consecutive slots of each segment. Slots past a
@@ -707,9 +710,14 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
       // Buckets above t end at or before the K-th slot; bucket t's segment
       // starts below it, so "slot < K" keeps exactly its first need keys.
       const uint32_t slot = rank[u];
-      if ((FULL || s0[u] < s1[u]) && slot < (uint32_t)K) {
-        if constexpr (W16) out.put_rj(slot, (uint32_t)me[u] >> 12, me[u]);
-        else out.put(slot, me[u]);
+      if constexpr (W16) {
+        if (direct) {
+          if (FULL || s0[u] < s1[u]) out.put_rj(ridx, rval, slot, (uint32_t)me[u] >> 12, me[u]);
+        } else if ((FULL || s0[u] < s1[u]) && slot < (uint32_t)K) {
+          out.put_key(slot, bucket_index_of(me[u]), me[u]);
+        }
+      } else if ((FULL || s0[u] < s1[u]) && slot < (uint32_t)K) {
+        out.put(slot, me[u]);
       }
     }
   };
