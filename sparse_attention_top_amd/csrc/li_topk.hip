@@ -118,19 +118,19 @@ __device__ inline unsigned long long composite(float s, int j) {
 
 __device__ inline int32_t index_of(unsigned long long c) { return (int32_t)(0xFFFFFFFFu - (uint32_t)c); }
 
-// The fast path's composite for rows of at most 2^20 keys also carries the
-// key's bucket b in the low 12 bits of its low word: (ord(score), 2^20-1-j, b).
-// s is canonical (as the score kernel stores it); rjs = (2^20-1-j) << 12.
-// Inside a bucket segment the order is the plain composite's (b is common);
-// a key of a lower bucket has a lower score, so its composite is lower whatever
-// its low word holds.
-constexpr uint32_t kIdxMask = (1u << 20) - 1;
+// The fast path's composite (rows of at most 65535 keys) also carries the
+// key's bucket b in the low 12 bits of its low word, the complemented index in
+// the high 16: (ord(score), 65535-j, b). s is canonical (as the score kernel
+// stores it); rjs = (65535-j) << 16. Inside a bucket segment the order is the
+// plain composite's (b is common); a key of a lower bucket has a lower score,
+// so its composite is lower whatever its low word holds.
+constexpr uint32_t kIdxMask = 0xFFFFu;
 __device__ inline unsigned long long bucket_composite(float s, int b, uint32_t rjs) {
   return ((unsigned long long)ord_bits(s) << 32) | (rjs + (uint32_t)b);
 }
 __device__ inline int bucket_of(unsigned long long c) { return (int)((uint32_t)c & 0xFFFu); }
 __device__ inline int32_t bucket_index_of(unsigned long long c) {
-  return (int32_t)(kIdxMask - ((uint32_t)c >> 12));
+  return (int32_t)(kIdxMask - ((uint32_t)c >> 16));
 }
 
 // Where a record's result goes: output slots idx[d] / val[d] (val may be null).
@@ -146,16 +146,15 @@ struct Out {
     idx[d] = (gather ? gather[j] : j) + off;
     if (val) val[d] = from_ord((uint32_t)(c >> 32));
   }
-  // Fast-path store from the complemented index r = 2^20-1-j (the composite's
-  // low word >> 12) through buffer records of k slots: a slot at or past k is
-  // dropped by the hardware, and j + off is one subtraction from a uniform
-  // constant (records without gather only).
+  // Fast-path store from the composite's low word lw (65535-j in its high
+  // half) through buffer records of k slots: a slot at or past k is dropped by
+  // the hardware, and j + off is one subtraction of lw's high half from a
+  // uniform constant (records without gather only).
   __device__ void put_rj(__amdgpu_buffer_rsrc_t ridx, __amdgpu_buffer_rsrc_t rval, uint32_t d,
-                         uint32_t r, unsigned long long c) const {
+                         uint32_t lw, unsigned long long c) const {
     int32_t v;
-    // kept as one subtraction (the compiler would otherwise form 2^20-1-r and
-    // add off to it)
-    asm("v_sub_u32 %0, %1, %2" : "=v"(v) : "s"(kIdxMask + (uint32_t)off), "v"(r));
+    asm("v_sub_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+        : "=v"(v) : "s"(kIdxMask + (uint32_t)off), "v"(lw));
     const int b = (int)(d * 4u);
     __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, ridx, b, 0, 0);
     if (val) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(from_ord((uint32_t)(c >> 32))), rval, b,
@@ -613,17 +612,17 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   // Zero composites past the candidates (the counting sort writes [0, ncand)).
   for (int e = tid; e < kBufPad; e += NT) sm.buf[ncand + e] = 0ull;
 
-  // (2^20-1-4*tid) << 12: key j = 4*tid + c of this thread has low word
-  // rjt - (c << 12) + b, one three-operand add (the empty asm keeps the base
+  // (65535-4*tid) << 16: key j = 4*tid + c of this thread has low word
+  // rjt - (c << 16) + b, one three-operand add (the empty asm keeps the base
   // in a register instead of being recomputed for every key).
-  uint32_t rjt = (kIdxMask - 4u * (uint32_t)tid) << 12;
+  uint32_t rjt = (kIdxMask - 4u * (uint32_t)tid) << 16;
   asm volatile("" : "+v"(rjt));
   // Counting sort of the keys of buckets >= t into their bucket segments.
   // Afterwards bucket b's segment is [end(b+1), end(b)) (end(nb) = 0: the zero
   // word past the buckets). The four atomics of a group are all issued before
   // their results are read.
   row.each4([&](const float (&x)[4], int j0, auto rng) {
-    const uint32_t rjs0 = rjt - (((uint32_t)j0 - 4u * (uint32_t)tid) << 12);
+    const uint32_t rjs0 = rjt - (((uint32_t)j0 - 4u * (uint32_t)tid) << 16);
     int b[4];
     bool c[4];
     uint32_t raw[4];
@@ -640,7 +639,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
       if (c[e]) {
         const uint32_t pos = cnt.field(raw[e], b[e]);
         if constexpr (W16)
-          at(pos) = bucket_composite(x[e], b[e], rjs0 - ((uint32_t)e << 12));
+          at(pos) = bucket_composite(x[e], b[e], rjs0 - ((uint32_t)e << 16));
         else
           at(pos) = composite(x[e], j0 + e);
       }
@@ -712,7 +711,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
       const uint32_t slot = rank[u];
       if constexpr (W16) {
         if (direct) {
-          if (FULL || s0[u] < s1[u]) out.put_rj(ridx, rval, slot, (uint32_t)me[u] >> 12, me[u]);
+          if (FULL || s0[u] < s1[u]) out.put_rj(ridx, rval, slot, (uint32_t)me[u], me[u]);
         } else if ((FULL || s0[u] < s1[u]) && slot < (uint32_t)K) {
           out.put_key(slot, bucket_index_of(me[u]), me[u]);
         }
