@@ -128,7 +128,8 @@ constexpr uint32_t kIdxMask = 0xFFFFu;
 __device__ inline unsigned long long bucket_composite(float s, int b, uint32_t rjs) {
   return ((unsigned long long)ord_bits(s) << 32) | (rjs + (uint32_t)b);
 }
-__device__ inline int bucket_of(unsigned long long c) { return (int)((uint32_t)c & 0xFFFu); }
+// (bits 12-15 are zero, so the low half is the bucket: one SDWA operand)
+__device__ inline int bucket_of(unsigned long long c) { return (int)((uint32_t)c & 0xFFFFu); }
 __device__ inline int32_t bucket_index_of(unsigned long long c) {
   return (int32_t)(kIdxMask - ((uint32_t)c >> 16));
 }
@@ -199,15 +200,13 @@ struct Counters {
     if constexpr (W16) return (word(b >> 1) >> ((b & 1) << 4)) & 0xFFFFu;
     else return word(b);
   }
-  // (get(b + 1), get(b)) from the two adjacent words that hold them.
+  // (get(b + 1), get(b)). For 16-bit counters these are the two consecutive
+  // halfwords at bytes 2b + 2 and 2b (little-endian halves), read as such.
   __device__ void get_pair(int b, uint32_t& up, uint32_t& at) const {
     if constexpr (W16) {
-      // (w1:w0) >> (16 * (b & 1)) holds (get(b + 1), get(b)) in its low word;
-      // v_alignbit_b32 reads only the low five bits of b << 4
-      const uint32_t w0 = word(b >> 1), w1 = word((b >> 1) + 1);
-      const uint32_t pair = __builtin_amdgcn_alignbit(w1, w0, (uint32_t)b << 4);
-      at = pair & 0xFFFFu;
-      up = pair >> 16;
+      const uint16_t* h = reinterpret_cast<const uint16_t*>(w);
+      at = h[b];
+      up = h[b + 1];
     } else {
       at = word(b);
       up = word(b + 1);
