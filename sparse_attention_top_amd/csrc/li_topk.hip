@@ -650,7 +650,10 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   const auto ridx = __builtin_amdgcn_make_buffer_rsrc(out.idx, (short)0, K * 4, kRsrcWord3);
   const auto rval = __builtin_amdgcn_make_buffer_rsrc(out.val, (short)0, out.val ? K * 4 : 0, kRsrcWord3);
   // Rank every grouped key inside its segment and store it at its sorted
-  // position. NB candidates per thread (slots p0 + u*NT) are ranked together;
+  // position. NB candidates per thread are ranked together: in a whole batch
+  // a wave takes 256 consecutive slots, lane l slots l + 64u (so a wave's
+  // loop, which runs to its longest segment, stays in one region of the
+  // buffer); in a remainder batch slot p0 is thread p0 - base's;
   // each step reads two consecutive slots of each segment. Slots past a
   // segment's end hold smaller composites (later segments, or the zero pad),
   // so they never count and need no mask. FULL: every slot is < ncand.
@@ -663,7 +666,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     uint32_t len = 0;
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      const uint32_t p = p0 + u * NT;
+      const uint32_t p = p0 + u * (NB > 1 ? 64u : (uint32_t)NT);
       me[u] = sm.buf[FULL || p < ncand ? p : 0];
     }
 #pragma unroll
@@ -675,7 +678,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
     // rank[u] starts at the segment's first slot, so it ends as the sorted slot
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      if (!FULL && p0 + u * NT >= ncand) s1[u] = s0[u];
+      if (!FULL && p0 + u * (NB > 1 ? 64u : (uint32_t)NT) >= ncand) s1[u] = s0[u];
       rank[u] = s0[u] / U;
       len = max(len, s1[u] - s0[u]);
     }
@@ -725,7 +728,7 @@ __device__ bool select_by_buckets(const Row<NT, R, RES, KEPT>& row, float lo, fl
   using std::integral_constant;
   uint32_t base = 0;
   for (; base + 4 * NT <= ncand; base += 4 * NT)
-    rank_batch(base + tid, integral_constant<int, 4>{}, integral_constant<bool, true>{});
+    rank_batch(base + 4 * (tid & ~63) + (tid & 63), integral_constant<int, 4>{}, integral_constant<bool, true>{});
   for (; base < ncand; base += NT)
     if (base + (tid & ~63) < ncand)   // uniform per wave
       rank_batch(base + tid, integral_constant<int, 1>{}, integral_constant<bool, false>{});
