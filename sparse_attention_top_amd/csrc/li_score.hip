@@ -131,6 +131,15 @@ __device__ inline float load_weight(const void* w, int dtype, int64_t i) {
   return (float)__builtin_bit_cast(_Float16, bits);
 }
 
+// The key-row swizzle of the score kernel's LDS tiles (see there), as a
+// compile-time function of the row for rows of ROW bytes.
+template <int ROW> constexpr int swz_of(int r) {
+  constexpr int U = ROW / 16;
+  constexpr int RPW = ROW >= 128 ? 1 : 128 / ROW;
+  const int x = r / RPW;
+  return (x ^ (x >> __builtin_ctz(U))) & (U - 1);
+}
+
 // Byte offset past any record count: the store is dropped (kRsrcWord3).
 constexpr int kDropOffset = (int)0x80000000u;
 
@@ -151,6 +160,15 @@ __device__ inline void lds_dma16(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(lds), "v"(gptr)
+               : "memory", "m0");
+}
+
+// The same from a wave-uniform base address plus a 32-bit per-lane byte offset
+// (the scalar-base form: no 64-bit address arithmetic per lane).
+__device__ inline void lds_dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
 
@@ -233,10 +251,7 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   // any 8 (and any 16) consecutive rows of such a read on distinct banks.
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[KBUF];
   __shared__ float ksc[2][QUANT ? KT : 1];
-  auto swz = [](int r) {
-    const int x = r / RPW;
-    return (x ^ (x >> LOG_U)) & (U - 1);
-  };
+  auto swz = [](int r) { return swz_of<ROW>(r); };
 
   // The LB-byte fragment at LDS byte base ^ (2*LB*s) (and ^16 for its second
   // 16-byte half).
@@ -287,10 +302,10 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)kbuf;
   // LDS byte (of the wave's d-th 1 KB block) this lane writes, and the key row
   // and byte within the row that belong there.
-  auto dma_row = [&](int d) { return ((d * NW + wave) * 1024 + lane * 16) / ROW; };
-  auto dma_byte = [&](int d) {
-    const int r = dma_row(d);
-    const int b = (lane * 16) % ROW;   // 1 KB blocks hold whole rows
+  auto dma_row = [&](int d, int ln) { return ((d * NW + wave) * 1024 + ln * 16) / ROW; };
+  auto dma_byte = [&](int d, int ln) {
+    const int r = dma_row(d, ln);
+    const int b = (ln * 16) % ROW;   // 1 KB blocks hold whole rows
     return ((b / 16) ^ swz(r)) * 16;
   };
   auto stage_key = [&](int st, int kk) { return min(it.k0 + st * KT + kk, jmax); };
@@ -309,25 +324,67 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     if (QUANT) psid = btab[block_index(stage_key(st, tid % KT))];
   };
   float pre_sc = 0.f;
+  // Within a contiguous stage, the lane's d-th 1 KB DMA block reads from byte
+  // (d * NW + wave) * 1024 + (dma_v ^ 16 * swz(R_d)), R_d = (d * NW + wave) *
+  // 1024 / ROW its first key row: 1 KB blocks hold whole rows, and the
+  // swizzle of a row R_d + l (l < 1024 / ROW, R_d a multiple of it) is
+  // swz(R_d) ^ swz(l) for every row size here, so the block's part of the
+  // source offset is a uniform XOR of the lane's offset in block 0.
+  const uint32_t dma_v = (uint32_t)((lane * 16 / ROW) * ROW +
+                                    ((((lane * 16) % ROW) / 16) ^ swz(lane * 16 / ROW)) * 16);
+  const auto ks_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.k_scale) + (QUANT ? br.k_base : 0), (short)0, QUANT ? br.s_k * 4 : 0,
+      kRsrcWord3);
   auto fetch = [&](int st) {
     const uint32_t lds = lds0 + (st & 1) * STAGE;
+    if (!paged && it.k0 + (st + 1) * KT <= it.k1) {   // uniform
+      // A whole contiguous stage (no key clamped): each block is a scalar base
+      // plus the lane's offset, one XOR per block. The opaque copy keeps the
+      // per-block offsets from being hoisted out of the stage loop (DPW more
+      // live registers).
+      const uint8_t* sb = a.k + ((int64_t)br.k_base + it.k0 + st * KT) * ROW;
+      uint32_t v = dma_v;
+      asm volatile("" : "+v"(v));
+#pragma unroll
+      for (int d = 0; d < DPW; ++d) {
+        const int blk = d * NW + wave;
+        lds_dma16_s(sb + blk * 1024, v ^ (16u * (uint32_t)swz(blk * (1024 / ROW))), lds + blk * 1024);
+      }
+      if (QUANT)
+        pre_sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            ks_rsrc, (uint32_t)(tid % KT) * 4u, (it.k0 + st * KT) * 4, 0));
+      return;
+    }
+    if (!paged) {
+      // The last stage of an item (keys clamped to its last key). The opaque
+      // lane keeps this path's per-block rows and bytes from being hoisted
+      // out of the stage loop, where they would hold registers for a path
+      // taken once per item.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int d = 0; d < DPW; ++d) {
+        const int64_t off = ((int64_t)br.k_base + stage_key(st, dma_row(d, ln))) * ROW;
+        lds_dma16(a.k + off + dma_byte(d, ln), lds + (d * NW + wave) * 1024);
+      }
+      if (QUANT) pre_sc = a.k_scale[(int64_t)br.k_base + stage_key(st, tid % KT)];
+      return;
+    }
+    // Paged keys: each block's source is its cache block's row. (The
+    // one-accumulator-set kernels have no registers to spare for hoisted lane
+    // offsets: opaque lane there too.)
+    int lp = lane;
+    if constexpr (!PP) asm volatile("" : "+v"(lp));
 #pragma unroll
     for (int d = 0; d < DPW; ++d) {
-      const int j = stage_key(st, dma_row(d));
-      int64_t off;
-      if (paged) {
-        const int bo = j - block_index(j) * a.block_size;
-        off = ((int64_t)clamp_block(pid[d]) * a.k_block_stride + (int64_t)bo * D) * ES;
-      } else {
-        off = ((int64_t)br.k_base + j) * ROW;
-      }
-      lds_dma16(a.k + off + dma_byte(d), lds + (d * NW + wave) * 1024);
+      const int j = stage_key(st, dma_row(d, lp));
+      const int bo = j - block_index(j) * a.block_size;
+      const int64_t off = ((int64_t)clamp_block(pid[d]) * a.k_block_stride + (int64_t)bo * D) * ES;
+      lds_dma16(a.k + off + dma_byte(d, lp), lds + (d * NW + wave) * 1024);
     }
     if (QUANT) {
       const int j = stage_key(st, tid % KT);
-      const int64_t off = paged ? (int64_t)clamp_block(psid) * a.block_size + (j - block_index(j) * a.block_size)
-                                : (int64_t)br.k_base + j;
-      pre_sc = a.k_scale[off];
+      pre_sc = a.k_scale[(int64_t)clamp_block(psid) * a.block_size + (j - block_index(j) * a.block_size)];
     }
   };
   auto stash_scales = [&](int st) {
@@ -484,6 +541,28 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   }
   // Dequant key scale of the next slice, read together with its B fragments.
   float ksn = QUANT ? ksc[0][wk * 32 + col] : 1.f;
+  // FIMM (one key slice per wave, WK == 1, so the slice of every unrolled step
+  // is known at compile time): the fragment reads take their slice and k-step
+  // from the instruction's immediate offset. The swizzle of row sub*32 + col is
+  // swz(col) ^ swz(sub*32), and the logical unit (2s + half)*NU + e is the XOR
+  // of its three bit fields, so the physical unit is
+  //   ((half*NU) ^ swz(col)) ^ q ^ swz(sub*32),   q = 2*NU*s + e,
+  // and XOR with swz(sub*32) permutes the KSTEPS*NU values of q among
+  // themselves. fa[m] holds the lane's byte address of value q_m (row col of
+  // slice 0, current buffer); a read adds the slice's rows as an immediate. The
+  // buffer offset moves with the stages (one add per register per stage, not
+  // an address computation per read).
+  constexpr int QM = KSTEPS * NU;
+  constexpr bool FIMM = WK == 1;
+  auto q_of = [](int m) { return 2 * NU * (m / NU) + m % NU; };
+  auto m_of = [](int q) { return (q / (2 * NU)) * NU + q % (2 * NU); };
+  uint32_t fa[FIMM ? QM : 1];
+  uint32_t ka = (uint32_t)col * 4u;   // byte of the lane's key scale in ksc (slice 0)
+  if constexpr (FIMM) {
+    const int pl = (half * NU) ^ swz(col);
+#pragma unroll
+    for (int m = 0; m < QM; ++m) fa[m] = (uint32_t)(col * ROW + 16 * (pl ^ q_of(m)));
+  }
   auto step = [&](int st, auto ic, Acc (&acc)[NT], const Acc (&old)[NT], float& ks) {
     constexpr int i = decltype(ic)::value;
     const int buf = st & 1;
@@ -493,7 +572,34 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     const int nbuf = (i + 1 < SPS) ? buf : (buf ^ 1);
     const int nsub = (i + 1 < SPS) ? wk + (i + 1) * WK : wk;
     const int nbase = frag_base(nbuf, nsub);
-    if (QUANT) ksn = ksc[nbuf][nsub * 32 + col];
+    constexpr int NSUB = (i + 1 < SPS) ? i + 1 : 0;   // FIMM (wk == 0)
+    if constexpr (FIMM) {
+      if constexpr (i + 1 == SPS) {   // the next slice is in the other buffer
+        const int dst = buf ? -STAGE : STAGE;
+#pragma unroll
+        for (int m = 0; m < QM; ++m) fa[m] += (uint32_t)dst;
+        if (QUANT) ka += (uint32_t)(buf ? -KT * 4 : KT * 4);
+      }
+      if (QUANT) ksn = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(&ksc[0][0]) +
+                                                       ka + NSUB * 32 * 4);
+    } else {
+      if (QUANT) ksn = ksc[nbuf][nsub * 32 + col];
+    }
+    // B fragment of k-step s of the next slice
+    auto next_frag = [&](int s) -> Frag {
+      if constexpr (FIMM) {
+        constexpr int SW = swz_of<ROW>(NSUB * 32);
+        i32x4_t h[NU];
+#pragma unroll
+        for (int e = 0; e < NU; ++e)
+          h[e] = *reinterpret_cast<const i32x4_t*>(&kbuf[fa[m_of(q_of(s * NU + e) ^ SW)] +
+                                                         NSUB * 32 * ROW]);
+        if constexpr (NU == 1) return __builtin_bit_cast(Frag, h[0]);
+        else return Frag{h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+      } else {
+        return read_frag(nbase, s);
+      }
+    };
     float p0 = 0.f, p1 = 0.f;
     if constexpr (!PP) {
       // One accumulator set (old aliases acc): the previous slice's epilogue
@@ -514,7 +620,7 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
       for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = M::mma(qf[t][s], bf[s], s == 0 ? M::zero() : acc[t]);
-        bf[s] = read_frag(nbase, s);
+        bf[s] = next_frag(s);
       }
       return p0 + p1;
     }
@@ -534,7 +640,7 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
         asm volatile("" : "+v"(p0), "+v"(p1));
         __builtin_amdgcn_sched_barrier(0);
       }
-      bf[s] = read_frag(nbase, s);
+      bf[s] = next_frag(s);
     }
     return p0 + p1;
   };
