@@ -222,7 +222,7 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   static_assert(KSTEPS >= 1 && ROW % (2 * LB) == 0, "head dim must fill whole k-steps");
   static_assert(STAGE % (1024 * NW) == 0, "every wave stages the same number of 1 KB blocks");
   static_assert((ROW & (ROW - 1)) == 0 && (U & (U - 1)) == 0 && NU * 16 == LB, "power-of-two rows");
-  static_assert(!QUANT || KT <= NTHR, "one thread per staged key scale");
+  static_assert(!QUANT || KT + 32 <= NTHR, "one thread per staged key scale and its copy");
   // Query rows of 256-byte heads (16-bit D = 128) are staged through LDS when
   // they fit beside one key stage (160 KB for one workgroup per CU, 80 KB for
   // two): QROW bytes per row (N1 <= 64). Loaded straight into A-operand
@@ -250,7 +250,11 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   // consecutive rows; with x = r / RPW, swz = (x ^ (x >> log2 U)) mod U puts
   // any 8 (and any 16) consecutive rows of such a read on distinct banks.
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[KBUF];
-  __shared__ float ksc[2][QUANT ? KT : 1];
+  // Key dequant scales of the two staged tiles, stage st at [(st & 1) * KT,
+  // +KT), and after them a copy of buffer 0's first 32: the scales of two
+  // consecutive 32-key slices then always lie side by side, also across the
+  // end of buffer 1.
+  __shared__ float ksc[QUANT ? 2 * KT + 32 : 1];
   auto swz = [](int r) { return swz_of<ROW>(r); };
 
   // The LB-byte fragment at LDS byte base ^ (2*LB*s) (and ^16 for its second
@@ -388,7 +392,9 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     }
   };
   auto stash_scales = [&](int st) {
-    if (QUANT && tid < KT) ksc[st & 1][tid] = pre_sc;
+    if (QUANT && tid < KT) ksc[(st & 1) * KT + tid] = pre_sc;
+    // threads KT .. KT+31 hold the scales of keys 0 .. 31 of the stage
+    if (QUANT && (st & 1) == 0 && tid >= KT && tid < KT + 32) ksc[2 * KT + tid - KT] = pre_sc;
   };
 
   const int nstages = (it.k1 - it.k0 + KT - 1) / KT;
@@ -540,7 +546,7 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     for (int s = 0; s < KSTEPS; ++s) bf[s] = read_frag(b0, s);
   }
   // Dequant key scale of the next slice, read together with its B fragments.
-  float ksn = QUANT ? ksc[0][wk * 32 + col] : 1.f;
+  float ksn = QUANT ? ksc[wk * 32 + col] : 1.f;
   // FIMM (one key slice per wave, WK == 1, so the slice of every unrolled step
   // is known at compile time): the fragment reads take their slice and k-step
   // from the instruction's immediate offset. The swizzle of row sub*32 + col is
@@ -554,6 +560,9 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   // an address computation per read).
   constexpr int QM = KSTEPS * NU;
   constexpr bool FIMM = WK == 1;
+  // FPAIR: two consecutive slices finish together (below) with one scale read
+  // and a store offset of one add; their scales are read per pair, not per slice.
+  constexpr bool FPAIR = FIMM && !BL;
   auto q_of = [](int m) { return 2 * NU * (m / NU) + m % NU; };
   auto m_of = [](int q) { return (q / (2 * NU)) * NU + q % (2 * NU); };
   uint32_t fa[FIMM ? QM : 1];
@@ -580,10 +589,10 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
         for (int m = 0; m < QM; ++m) fa[m] += (uint32_t)dst;
         if (QUANT) ka += (uint32_t)(buf ? -KT * 4 : KT * 4);
       }
-      if (QUANT) ksn = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(&ksc[0][0]) +
-                                                       ka + NSUB * 32 * 4);
+      if (QUANT && !FPAIR)
+        ksn = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ksc) + ka + NSUB * 32 * 4);
     } else {
-      if (QUANT) ksn = ksc[nbuf][nsub * 32 + col];
+      if (QUANT) ksn = ksc[nbuf * KT + nsub * 32 + col];
     }
     // B fragment of k-step s of the next slice
     auto next_frag = [&](int s) -> Frag {
@@ -704,6 +713,26 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rsrc, off, 0, 0);
   };
 
+  // FPAIR: the same for slices A and B = A + 1 (keys kba and kba + 32), with
+  // lane l's key scale read by the caller (ksc bytes of A's first key + 4 l)
+  // and lane l's key kba + l; VALID = false drops slice A's half (the first
+  // pair of an item, whose slice A does not exist).
+  auto finish_pair = [&](float pa, float pb, int kba, float ks, auto valid_tag) {
+    constexpr bool VALID = decltype(valid_tag)::value;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb),
+                                                     false, false);
+    float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    tot = QUANT ? fmaf(tot, ks, 0.0f) : tot + 0.0f;   // canonical: never -0
+    int off = (kba + lane) * 4;
+    if constexpr (!VALID) off = half ? off : kDropOffset;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rsrc, off, 0, 0);
+  };
+  auto pair_scale = [&](int sbyte) {   // sbyte: ksc byte of slice A's first key
+    return QUANT ? *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ksc) + sbyte +
+                                                   lane * 4)
+                 : 1.f;
+  };
+
   // PP: even slices of a stage accumulate in acc0, odd ones in acc1; else all
   // in acc0. The first slice's (dropped) epilogue reads zeros.
   Acc acc0[NT], acc1[NT];
@@ -713,6 +742,10 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     if (!PP) acc0[t] = M::zero();
   }
   float ks0 = 1.f, ks1 = 1.f;
+  // FPAIR: scales of the first pair of the coming stage (stage 0: slice A
+  // absent, slice B = stage 0's first, from the copy after buffer 1)
+  float kspx = 1.f;
+  if constexpr (FPAIR) kspx = pair_scale((KT + (SPS - 1) * 32) * 4);
   float hp = 0.f, hks = 1.f;   // an even slice's part, finished with the next one
   int hkb = 0;
   bool hvalid = false;
@@ -727,6 +760,11 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
         else stage_barrier<SPS / 2>();
         if (st + 2 < nstages) fetch(st + 2);
         if (st + 3 < nstages) ids(st + 3);
+        // Scales of the pair (this stage's last slice, the next stage's
+        // first): the next stage's are published by the barrier above, and
+        // this stage's buffer is refilled (stash before the next stage's
+        // barrier) while slower waves may still finish that pair: read now.
+        if constexpr (FPAIR) kspx = pair_scale(((st & 1) * KT + (SPS - 1) * 32) * 4);
       }
       // previous slice: (st, i-1), or the last slice of stage st-1
       const int pkb = i > 0 ? slice_key(st, i - 1) : slice_key(st - 1, SPS - 1);
@@ -735,11 +773,23 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
         hkb = pkb;
         hks = ks1;
         hvalid = i > 0 || st > 0;
+      } else if constexpr (FPAIR) {
+        // slice A = i - 2 of this stage, or (i = 1) the last of the previous
+        // one, whose scales were read before they could be overwritten
+        const float ksp = i >= 2 ? pair_scale(((st & 1) * KT + (i - 2) * 32) * 4) : kspx;
+        const float part = PP ? step(st, ic, acc1, acc0, ks1) : step(st, ic, acc0, acc0, ks1);
+        if (i == 1 && st == 0)
+          finish_pair(hp, part, hkb, ksp, std::false_type{});
+        else
+          finish_pair(hp, part, hkb, ksp, std::true_type{});
       } else {
         const float part = PP ? step(st, ic, acc1, acc0, ks1) : step(st, ic, acc0, acc0, ks1);
         finish2(hp, hkb, hks, hvalid, part, pkb, ks0);
       }
     });
+  }
+  if constexpr (FPAIR) {
+    if (QUANT) ks1 = ksc[((nstages - 1) & 1) * KT + (SPS - 1) * 32 + col];
   }
   finish(epi(PP ? acc1 : acc0), slice_key(nstages - 1, SPS - 1), ks1, true);
 }
