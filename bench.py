@@ -27,7 +27,10 @@ to under load; a few steps after a cold start read 2-3% slower.
 Cold timings (`cold` in the JSON line): each kernel is also launched
 --cold-reps times right after a 512 MiB fill kernel that evicts the Infinity
 Cache and every L2, HIP events on the launch stream around the kernel alone;
-the median is reported with the HBM fraction it implies. `measured_peaks`
+the median is reported with the HBM fraction it implies. `launch_stats` gives
+the median, p10 and p90 of per-launch times, warm (--launch-reps launches of
+each kernel back to back, each between its own HIP events) and cold (the
+launches above). `measured_peaks`
 gives this box's own device-copy rate and hipBLASLt bf16 GEMM rate (torch
 library calls, context for the spec peaks only).
 """
@@ -116,6 +119,8 @@ def main():
                     help="launch every step eagerly instead of replaying captured graphs")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="launches of each kernel timed after a 512 MiB cache flush (0: none)")
+    ap.add_argument("--launch-reps", type=int, default=50,
+                    help="warm launches of each kernel timed one by one (median, p10, p90; 0: none)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the on-box reference rates (device copy, bf16 GEMM)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -228,6 +233,31 @@ def main():
     print(f"[bench] timed {K} steps: {ms_per_step:.3f} ms/step (score {score_ms:.3f}, "
           f"top-k {topk_ms:.3f})", flush=True, file=sys.stderr)
 
+    # Per-launch distributions (median, p10, p90): each launch
+    # bracketed by its own HIP events on the launch stream, warm (back to back
+    # after the graphs) and cold (below).
+    def launch_times(fn, reps, flush=None):
+        ts = []
+        for r in range(reps):
+            if flush is not None:
+                flush.fill_(float(r))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return ts
+
+    def quantiles(ts):
+        v = sorted(ts)
+        q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))]
+        return {"median": round(q(0.5), 4), "p10": round(q(0.1), 4), "p90": round(q(0.9), 4)}
+
+    warm = None
+    if args.launch_reps > 0:
+        warm = {"score": launch_times(score, args.launch_reps), "topk": launch_times(topk, args.launch_reps)}
+
     # Cold timings: each launch follows a 512 MiB fill kernel (twice the 256 MB
     # Infinity Cache plus every L2), so its inputs come from HBM; HIP events on
     # the launch stream bracket the kernel alone. Median over the launches.
@@ -235,20 +265,10 @@ def main():
     if args.cold_reps > 0:
         flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
 
-        def cold_ms(fn):
-            ts = []
-            for r in range(args.cold_reps):
-                flush.fill_(float(r))
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            ts.sort()
-            return ts[len(ts) // 2]
-
-        cold = {"score_ms": cold_ms(score), "topk_ms": cold_ms(topk)}
+        cold = {"score": launch_times(score, args.cold_reps, flush),
+                "topk": launch_times(topk, args.cold_reps, flush)}
+        cold["score_ms"] = quantiles(cold["score"])["median"]
+        cold["topk_ms"] = quantiles(cold["topk"])["median"]
         del flush
         print(f"[bench] cold (after a 512 MiB flush): score {cold['score_ms']:.3f} ms, "
               f"top-k {cold['topk_ms']:.3f} ms", flush=True, file=sys.stderr)
@@ -353,6 +373,15 @@ def main():
                        "topk_frac_hbm_peak": round(tbytes / (cold["topk_ms"] * 1e-3) / 1e9 /
                                                    PEAK_HBM_GBS, 4),
                        "flush_bytes": 1 << 29, "launches": args.cold_reps, "timing": "eager, median"}
+    if warm is not None or cold is not None:
+        ls = {"timing": "eager, HIP events around each launch"}
+        if warm is not None:
+            ls["warm"] = {"launches": args.launch_reps, "score_ms": quantiles(warm["score"]),
+                          "topk_ms": quantiles(warm["topk"])}
+        if cold is not None:
+            ls["cold"] = {"launches": args.cold_reps, "score_ms": quantiles(cold["score"]),
+                          "topk_ms": quantiles(cold["topk"])}
+        out["launch_stats"] = ls
     if peaks is not None:
         out["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
