@@ -135,7 +135,7 @@ __device__ inline float load_weight(const void* w, int dtype, int64_t i) {
 // compile-time function of the row for rows of ROW bytes.
 template <int ROW> constexpr int swz_of(int r) {
   constexpr int U = ROW / 16;
-  constexpr int RPW = ROW >= 128 ? 1 : 128 / ROW;
+  constexpr int RPW = ROW >= 128 ? 1 : 128 / ROW;   // key rows per 128-byte bank window
   const int x = r / RPW;
   return (x ^ (x >> __builtin_ctz(U))) & (U - 1);
 }
@@ -212,9 +212,7 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   constexpr int DMA = STAGE / 1024;        // 1 KB wave loads per stage
   constexpr int DPW = DMA / NW;            // ... per wave
   constexpr int U = ROW / 16;              // 16-byte swizzle units per key row
-  constexpr int LOG_U = __builtin_ctz(U);
   constexpr int NU = LB / 16;              // units per lane fragment (1 or 2)
-  constexpr int RPW = ROW >= 128 ? 1 : 128 / ROW;   // key rows per 128-byte bank window
   constexpr bool QUANT = (DT == LI_DTYPE_E4M3FN) || (DT == LI_DTYPE_I8);
   constexpr int SPS = KT / 32 / WK;        // 32-key slices per staged tile per wave
   constexpr int EPM = 16 / KSTEPS;         // previous-slice accumulators per MFMA
@@ -620,10 +618,12 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
 #pragma unroll
           for (int u = 0; u < EPM; u += 2) {
             const int e = s * EPM + u;
+            // one chain (a second would cost an add per slice; the other
+            // waves hide the chain's latency)
             p0 = fmaf(wr[t][e], M::relu(old[t], e), p0);
-            p1 = fmaf(wr[t][e + 1], M::relu(old[t], e + 1), p1);
+            p0 = fmaf(wr[t][e + 1], M::relu(old[t], e + 1), p0);
           }
-      asm volatile("" : "+v"(p0), "+v"(p1));
+      asm volatile("" : "+v"(p0));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
@@ -631,7 +631,7 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
         for (int t = 0; t < NT; ++t) acc[t] = M::mma(qf[t][s], bf[s], s == 0 ? M::zero() : acc[t]);
         bf[s] = next_frag(s);
       }
-      return p0 + p1;
+      return p0;
     }
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
@@ -666,9 +666,10 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
         for (int u = 0; u < EPM; u += 2) {
           const int e = s * EPM + u;
           p0 = fmaf(wr[t][e], M::relu(acc[t], e), p0);
-          p1 = fmaf(wr[t][e + 1], M::relu(acc[t], e + 1), p1);
+          if constexpr (PP) p1 = fmaf(wr[t][e + 1], M::relu(acc[t], e + 1), p1);
+          else p0 = fmaf(wr[t][e + 1], M::relu(acc[t], e + 1), p0);
         }
-    return p0 + p1;
+    return PP ? p0 + p1 : p0;
   };
   // Cross-half swap-add (both halves end up with the full sum over heads) and
   // the store of the slice starting at key kb by the lower half-wave; keys at
@@ -717,13 +718,14 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   // lane l's key scale read by the caller (ksc bytes of A's first key + 4 l)
   // and lane l's key kba + l; VALID = false drops slice A's half (the first
   // pair of an item, whose slice A does not exist).
+  const int lane4 = lane * 4;
   auto finish_pair = [&](float pa, float pb, int kba, float ks, auto valid_tag) {
     constexpr bool VALID = decltype(valid_tag)::value;
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb),
                                                      false, false);
     float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     tot = QUANT ? fmaf(tot, ks, 0.0f) : tot + 0.0f;   // canonical: never -0
-    int off = (kba + lane) * 4;
+    int off = lane4 + kba * 4;
     if constexpr (!VALID) off = half ? off : kDropOffset;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), out_rsrc, off, 0, 0);
   };
