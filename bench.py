@@ -31,8 +31,8 @@ the median is reported with the HBM fraction it implies. `launch_stats` gives
 the median, p10 and p90 of per-launch times, warm (--launch-reps launches of
 each kernel back to back, each between its own HIP events) and cold (the
 launches above). `measured_peaks`
-gives this box's own device-copy rate and hipBLASLt bf16 GEMM rate (torch
-library calls, context for the spec peaks only).
+gives this box's own device-copy rate and hipBLASLt bf16 and fp8 GEMM rates
+(torch library calls, context for the spec peaks only).
 """
 import argparse
 import hashlib
@@ -298,6 +298,19 @@ def main():
         t_gemm = rate(lambda: torch.matmul(m, n), 10)
         peaks = {"device_copy_gbs": round(2 * a.numel() * 4 / t_copy / 1e9, 1),
                  "bf16_gemm_tflops": round(2 * 8192 ** 3 / t_gemm / 1e12, 1)}
+        # fp8 (e4m3fn) GEMM through torch's scaled matmul, the same shape; null
+        # where this torch build has no such path.
+        try:
+            m8 = m.to(torch.float8_e4m3fn)
+            n8 = n.t().contiguous().to(torch.float8_e4m3fn).t()   # column-major right operand
+            one = torch.ones((), device=dev, dtype=torch.float32)
+            t_f8 = rate(lambda: torch._scaled_mm(m8, n8, scale_a=one, scale_b=one,
+                                                 out_dtype=torch.bfloat16), 10)
+            peaks["fp8_gemm_tflops"] = round(2 * 8192 ** 3 / t_f8 / 1e12, 1)
+            del m8, n8
+        except (RuntimeError, AttributeError, TypeError) as e:
+            print(f"[bench] fp8 GEMM rate unavailable ({e})", flush=True, file=sys.stderr)
+            peaks["fp8_gemm_tflops"] = None
         del a, b, m, n
 
     if args.copy_calibration:
