@@ -236,6 +236,27 @@ def test_edge_cases_all_rows(name):
     run_and_check(wl, label=name)
 
 
+@pytest.mark.parametrize("qk,layout_k", [("e4m3fn", "TND"), ("i8", "TND"),
+                                          ("e4m3fn", "PA_BSND")])
+def test_quant_key_scales_spread(qk, layout_k):
+    """Key dequant scales spread key by key over 2^-6 .. 2^6 (the codes are
+    unchanged, so the inputs stay valid): a key scored with another key's scale
+    (within a pair of 32-key slices, across a stage boundary, in an item's last
+    stage) lands far outside the error budget. Sequences of one to five
+    128-key stages, whole and partial last stages, and more than four query rows
+    (the fp8 / int8 prefill kernel) next to short ones."""
+    layout_q = "TND" if layout_k == "TND" else "BSND"
+    kw = dict(layout_q=layout_q, layout_k=layout_k, qk_dtype=qk, w_dtype="f32", N1=64,
+              D=128, seqlens_q=[9, 3, 17, 6], seqlens_k=[128, 200, 640, 37],
+              sparse_count=48, sparse_mode=3, seed=zlib.crc32(f"spread{qk}{layout_k}".encode()))
+    if layout_k == "PA_BSND":
+        kw["block_size"] = 64
+    wl = synth.build("quant_scale_spread", **kw)
+    rng = np.random.default_rng(kw["seed"])
+    wl.k_scale = (wl.k_scale * np.exp2(rng.integers(-6, 7, wl.k_scale.shape))).astype(np.float32)
+    run_and_check(wl, label=f"quant_scale_spread[{qk},{layout_k}]")
+
+
 def _random_case(seed):
     """A seeded random problem inside the documented limits: layout, dtypes, head
     count, head dim, lengths (empty and ragged included), mode, k, compressed
