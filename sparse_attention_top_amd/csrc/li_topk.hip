@@ -831,11 +831,19 @@ __device__ void select_by_radix(const Row<NT, R, RES, KEPT>& row, int K, int m, 
 // W16 (16-bit bucket counters) is used only for rows of at most 65535 keys.
 // A row's latency is a chain of dependent LDS and memory steps, so throughput
 // comes from rows in flight: the 256-thread kernel (every row up to 8K keys, in
-// one launch) is held to the register budget of six workgroups per CU (80
-// VGPRs; its LDS, about 25 KB, fits six in 160 KB; only the radix fallback
-// spills a few registers).
+// one launch) is held to the register budget of six waves per SIMD, i.e. six
+// workgroups per CU (80 VGPRs; its LDS, about 25 KB, fits six in 160 KB; only
+// the radix fallback spills a few registers), and the 512-thread kernel (rows
+// of 8K-16K keys) to the same six waves, three workgroups per CU (it would
+// otherwise take 107 VGPRs and run two: 13% slower on a 16-sequence fp8
+// prefill). Explicit attributes: a launch bound's minimum block count did not
+// cap the 512-thread kernel's registers.
 template <int NT, int R, bool RES, bool KEPT, bool W16, int KMAX>
-__global__ __launch_bounds__(NT, (NT == 256 && KMAX == kMaxKSmall) ? 6 : 1)
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NT),
+                          amdgpu_waves_per_eu(KMAX == kMaxKSmall &&
+                                                      (NT == 256 || (NT == 512 && !KEPT))
+                                                  ? 6
+                                                  : 1)))
 void topk_kernel(TopkArgs a, int first) {
   __shared__ Smem<NT, W16, KMAX> sm;
   const RowRec rr = a.rows[first + blockIdx.x];
