@@ -248,11 +248,14 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   // consecutive rows; with x = r / RPW, swz = (x ^ (x >> log2 U)) mod U puts
   // any 8 (and any 16) consecutive rows of such a read on distinct banks.
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[KBUF];
-  // Key dequant scales of the two staged tiles, stage st at [(st & 1) * KT,
-  // +KT), and after them a copy of buffer 0's first 32: the scales of two
-  // consecutive 32-key slices then always lie side by side, also across the
-  // end of buffer 1.
-  __shared__ float ksc[QUANT ? 2 * KT + 32 : 1];
+  // Key dequant scales in a ring of three stages, stage st at
+  // [(st % 3) * KT, +KT), and after them a copy of ring slot 0's first 32: the
+  // scales of two consecutive 32-key slices then always lie side by side,
+  // also across the end of the ring. Three slots, not two: stage st + 3 is
+  // stashed before the barrier ending stage st + 2, and a wave can be one
+  // barrier behind the others, so stage st's scales stay readable through
+  // stage st + 1 (pairs of slices read them after the barrier ending stage st).
+  __shared__ float ksc[QUANT ? 3 * KT + 32 : 1];
   auto swz = [](int r) { return swz_of<ROW>(r); };
 
   // The LB-byte fragment at LDS byte base ^ (2*LB*s) (and ^16 for its second
@@ -390,9 +393,10 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     }
   };
   auto stash_scales = [&](int st) {
-    if (QUANT && tid < KT) ksc[(st & 1) * KT + tid] = pre_sc;
+    const int sr = st % 3;   // ring slot (uniform)
+    if (QUANT && tid < KT) ksc[sr * KT + tid] = pre_sc;
     // threads KT .. KT+31 hold the scales of keys 0 .. 31 of the stage
-    if (QUANT && (st & 1) == 0 && tid >= KT && tid < KT + 32) ksc[2 * KT + tid - KT] = pre_sc;
+    if (QUANT && sr == 0 && tid >= KT && tid < KT + 32) ksc[3 * KT + tid - KT] = pre_sc;
   };
 
   const int nstages = (it.k1 - it.k0 + KT - 1) / KT;
@@ -564,7 +568,6 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
   auto q_of = [](int m) { return 2 * NU * (m / NU) + m % NU; };
   auto m_of = [](int q) { return (q / (2 * NU)) * NU + q % (2 * NU); };
   uint32_t fa[FIMM ? QM : 1];
-  uint32_t ka = (uint32_t)col * 4u;   // byte of the lane's key scale in ksc (slice 0)
   if constexpr (FIMM) {
     const int pl = (half * NU) ^ swz(col);
 #pragma unroll
@@ -585,13 +588,10 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
         const int dst = buf ? -STAGE : STAGE;
 #pragma unroll
         for (int m = 0; m < QM; ++m) fa[m] += (uint32_t)dst;
-        if (QUANT) ka += (uint32_t)(buf ? -KT * 4 : KT * 4);
       }
-      if (QUANT && !FPAIR)
-        ksn = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ksc) + ka + NSUB * 32 * 4);
-    } else {
-      if (QUANT) ksn = ksc[nbuf * KT + nsub * 32 + col];
     }
+    // scale of the next slice (stage st, or st + 1 for the last slice)
+    if (QUANT && !FPAIR) ksn = ksc[((i + 1 < SPS ? st : st + 1) % 3) * KT + nsub * 32 + col];
     // B fragment of k-step s of the next slice
     auto next_frag = [&](int s) -> Frag {
       if constexpr (FIMM) {
@@ -744,10 +744,6 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     if (!PP) acc0[t] = M::zero();
   }
   float ks0 = 1.f, ks1 = 1.f;
-  // FPAIR: scales of the first pair of the coming stage (stage 0: slice A
-  // absent, slice B = stage 0's first, from the copy after buffer 1)
-  float kspx = 1.f;
-  if constexpr (FPAIR) kspx = pair_scale((KT + (SPS - 1) * 32) * 4);
   float hp = 0.f, hks = 1.f;   // an even slice's part, finished with the next one
   int hkb = 0;
   bool hvalid = false;
@@ -762,11 +758,6 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
         else stage_barrier<SPS / 2>();
         if (st + 2 < nstages) fetch(st + 2);
         if (st + 3 < nstages) ids(st + 3);
-        // Scales of the pair (this stage's last slice, the next stage's
-        // first): the next stage's are published by the barrier above, and
-        // this stage's buffer is refilled (stash before the next stage's
-        // barrier) while slower waves may still finish that pair: read now.
-        if constexpr (FPAIR) kspx = pair_scale(((st & 1) * KT + (SPS - 1) * 32) * 4);
       }
       // previous slice: (st, i-1), or the last slice of stage st-1
       const int pkb = i > 0 ? slice_key(st, i - 1) : slice_key(st - 1, SPS - 1);
@@ -777,8 +768,10 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
         hvalid = i > 0 || st > 0;
       } else if constexpr (FPAIR) {
         // slice A = i - 2 of this stage, or (i = 1) the last of the previous
-        // one, whose scales were read before they could be overwritten
-        const float ksp = i >= 2 ? pair_scale(((st & 1) * KT + (i - 2) * 32) * 4) : kspx;
+        // one (ring slot (st + 2) % 3; for stage 0 a slot whose lanes are
+        // dropped, followed by the copy of stage 0's first 32)
+        const float ksp = pair_scale(
+            ((i >= 2 ? (st % 3) * KT + (i - 2) * 32 : ((st + 2) % 3) * KT + (SPS - 1) * 32)) * 4);
         const float part = PP ? step(st, ic, acc1, acc0, ks1) : step(st, ic, acc0, acc0, ks1);
         if (i == 1 && st == 0)
           finish_pair(hp, part, hkb, ksp, std::false_type{});
@@ -791,7 +784,7 @@ __global__ __launch_bounds__(WQ * WK * 64, MINB) void score_kernel(ScoreArgs a) 
     });
   }
   if constexpr (FPAIR) {
-    if (QUANT) ks1 = ksc[((nstages - 1) & 1) * KT + (SPS - 1) * 32 + col];
+    if (QUANT) ks1 = ksc[((nstages - 1) % 3) * KT + (SPS - 1) * 32 + col];
   }
   finish(epi(PP ? acc1 : acc0), slice_key(nstages - 1, SPS - 1), ks1, true);
 }
