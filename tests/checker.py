@@ -76,7 +76,10 @@ class RowStats:
     the floor 2^-6 M were dropped (tau = tol * |s_(k)|): floor_sel for the
     selection (rules 2-4), floor_val for the values (rule 5; a value near zero
     whose terms cancel has a large error relative to itself, which the float32
-    budget above bounds instead)."""
+    budget above bounds instead), and budget_val: values outside even the
+    floored relative band but inside the float32 budget, i.e. scores that are
+    cancellation residues finer than float32 resolves at the size of their own
+    terms (a row whose largest magnitude M is itself such a residue)."""
 
     def __init__(self):
         self.rows = 0
@@ -87,12 +90,13 @@ class RowStats:
         self.max_err_m = 0.0
         self.floor_sel = 0
         self.floor_val = 0
+        self.budget_val = 0
 
     def __repr__(self):
         return (f"rows={self.rows} exact_set={self.exact_set} tie_band={self.in_band} "
                 f"all_keys={self.all_keys} max_err/(u*P)={self.max_err_u:.3g} "
                 f"max_err/M={self.max_err_m:.3g} floor_sel={self.floor_sel} "
-                f"floor_val={self.floor_val}")
+                f"floor_val={self.floor_val} budget_val={self.budget_val}")
 
 
 def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: int,
@@ -153,6 +157,13 @@ def check_row(gidx: np.ndarray, gval: Optional[np.ndarray], s: np.ndarray, k: in
         assert np.isneginf(vt).all(), f"{where}: value tail must be -inf"
         err = np.abs(v - sh)
         lim = tol * np.maximum(np.abs(sh), floor)
+        if mag is not None and budget is not None:
+            # A value within the float32 error bound of its own terms is accepted
+            # where the relative band is finer than float32 resolves.
+            blim = budget * U32 * np.asarray(mag, np.float64)[head]
+            if stats is not None and ((err > lim) & (err <= blim)).any():
+                stats.budget_val += 1
+            lim = np.maximum(lim, blim)
         assert (err <= lim).all(), f"{where}: values off by up to {err.max():.3g} " \
                                    f"(limit {lim[np.argmax(err - lim)]:.3g})"
         assert (np.diff(v) <= 0).all(), f"{where}: values not non-increasing"
@@ -218,8 +229,10 @@ def _split_kept(g, gv, s, o, f, k, tol, where, mag=None, budget=None):
     floor = 2.0 ** -6 * np.abs(s).max()
     if gv is not None:
         err = np.abs(gv[:f] - s[g[:f]])
-        assert (err <= tol * np.maximum(np.abs(s[g[:f]]), floor)).all(), \
-            f"{where}: kept block values off by {err.max():.3g}"
+        lim = tol * np.maximum(np.abs(s[g[:f]]), floor)
+        if mag is not None and budget is not None:   # as in check_row
+            lim = np.maximum(lim, budget * U32 * np.asarray(mag, np.float64)[g[:f]])
+        assert (err <= lim).all(), f"{where}: kept block values off by {err.max():.3g}"
         if mag is not None and budget is not None:
             assert (err <= budget * U32 * np.asarray(mag)[g[:f]]).all(), \
                 f"{where}: kept block values outside the float32 error budget"

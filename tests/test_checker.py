@@ -104,3 +104,26 @@ def test_float32_error_budget():
     assert abs(bad[3] - s[head[3]]) < TOL * abs(s[head[3]])
     with pytest.raises(AssertionError):
         check_row(idx, bad, s, 10, TOL, mag=p, budget=392)
+
+
+def test_cancellation_residue_row_uses_the_budget():
+    """A row whose every score is a residue of cancelling terms (largest
+    magnitude 4e-5 from terms summing to 49 in magnitude; float32 resolves
+    49 * 2^-24 = 2.9e-6 there): a value off by 6.7e-8 fails the relative band
+    with its floor (1e-3 * max(|s|, 2^-6 M) = 3.9e-8) but lies within 0.03 units
+    of 2^-24 P_j and passes; off by more than the budget it still fails."""
+    from tests.checker import U32, RowStats
+    s = np.array([0.0, -3.889e-5, -3.95e-5, -4.0e-5])
+    p = np.full(4, 49.0)
+    idx = np.array([0, 1, 2, 3])
+    val = s.copy()
+    val[1] += 6.7e-8
+    st = RowStats()
+    check_row(idx, val, s, 4, TOL, mag=p, budget=266, stats=st)
+    assert st.budget_val == 1
+    with pytest.raises(AssertionError):   # without the budget the band alone rejects it
+        check_row(idx, val, s, 4, TOL)
+    bad = s.copy()
+    bad[3] -= 300 * U32 * 49.0            # still the smallest value: only the budget fails
+    with pytest.raises(AssertionError, match="budget|values off"):
+        check_row(idx, bad, s, 4, TOL, mag=p, budget=266)
